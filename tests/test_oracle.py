@@ -1,0 +1,353 @@
+"""Pins for the fp64 oracle, checked against things other than the oracle itself.
+
+Each test names what it pins and which plausible mistake it would catch:
+  * the dense definition and lambda = 0 against SciPy's softmax / logsumexp and torch's
+    scaled_dot_product_attention in float64 (catches a transposed operand, a wrong scale, a
+    dropped rescale of l or O, an off-by-one causal mask, a wrong GQA head map);
+  * the streaming loop at lambda > 0 against the closed form "softmax over the kept tiles,
+    normalised with the global row max", whose kept set comes from prefix maxima of the tile
+    maxima (catches a wrong running max, a wrong sign or direction in the test, a skipped tile
+    that still adds to l or O);
+  * a hand-derived worked example (tests/golden/hand_tiles.json) for the "every row" vote, the
+    strict comparison and the ragged last tile;
+  * invariants fixed by the pages: the test's left side lies in (0, 1], lambda = 0 skips nothing,
+    the skipped count is monotone in lambda, and the approximation error is bounded by the
+    skipped mass.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp, softmax
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _masked_scores(q, k, row_keys, scale):
+    s = scale * (q @ k.T)
+    mask = np.arange(k.shape[0])[None, :] >= np.asarray(row_keys)[:, None]
+    s = np.where(mask, -np.inf, s)
+    return s
+
+
+def _library_attention(q, k, v, row_keys, scale):
+    s = _masked_scores(q, k, row_keys, scale)
+    return softmax(s, axis=1) @ v, logsumexp(s, axis=1)
+
+
+def _clustered_rows(rng, n_rows, n_keys, d, d_v, beta, cluster=16):
+    centres = rng.standard_normal((n_keys // cluster + 1, d)) * beta / math.sqrt(d)
+    idx = np.arange(n_keys) // cluster
+    k = 3 * centres[idx] + 0.5 * rng.standard_normal((n_keys, d))
+    qi = rng.integers(0, n_keys, size=n_rows)
+    q = centres[idx[qi]] + 0.5 * rng.standard_normal((n_rows, d))
+    v = rng.standard_normal((n_keys, d_v))
+    return q, k, v
+
+
+def _closed_form(q, k, v, row_keys, scale, lam, block_c, k_begin=0, k_end=None):
+    """Kept set from prefix maxima of tile maxima; output = softmax over the kept keys."""
+    n_keys = k.shape[0] if k_end is None else k_end
+    s = _masked_scores(q, k[:n_keys], row_keys, scale)[:, k_begin:n_keys]
+    n = s.shape[1]
+    tiles = [(a, min(a + block_c, n)) for a in range(0, n, block_c)]
+    tmax = np.stack([s[:, a:e].max(axis=1) for a, e in tiles], axis=1)  # rows x tiles
+    prefix = np.maximum.accumulate(tmax, axis=1)  # running max including the tile
+    with np.errstate(invalid="ignore"):
+        row_margin = np.where(np.isfinite(tmax), tmax - prefix, -np.inf)
+    visited = np.isfinite(tmax).any(axis=0)
+    margin = row_margin.max(axis=0)
+    tau = -np.inf if lam == 0 else math.log(min(lam, 1.0))
+    skipped = visited & (margin < tau)
+    keep_cols = np.zeros(n, dtype=bool)
+    for t, (a, e) in enumerate(tiles):
+        if visited[t] and not skipped[t]:
+            keep_cols[a:e] = True
+    sk = np.where(keep_cols[None, :], s, -np.inf)
+    o = softmax(sk, axis=1) @ v[k_begin:n_keys]
+    return dict(o=o, lse=logsumexp(sk, axis=1), margin=margin, visited=visited, skipped=skipped,
+                s=s, keep_cols=keep_cols)
+
+
+# ------------------------------------------------------------------------------------------
+# Dense definition and lambda = 0
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n_keys,causal", [(1, False), (37, False), (130, True), (200, False)])
+def test_dense_rows_match_scipy(n_keys, causal):
+    rng = np.random.default_rng(n_keys)
+    n_rows, d, dv = 9, 16, 12
+    q = rng.standard_normal((n_rows, d))
+    k = rng.standard_normal((n_keys, d))
+    v = rng.standard_normal((n_keys, dv))
+    row_keys = [max(1, n_keys - 3 * r) for r in range(n_rows)] if causal else [n_keys] * n_rows
+    scale = 0.3
+    o, lse = oracle.dense_rows(q, k, v, row_keys, scale)
+    o_ref, lse_ref = _library_attention(q, k, v, row_keys, scale)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("block_c", [1, 7, 16, 64, 500])
+def test_lambda_zero_equals_dense(block_c):
+    rng = np.random.default_rng(block_c)
+    q, k, v = _clustered_rows(rng, 11, 203, 24, 8, beta=6.0)
+    row_keys = [203 - 17 * r for r in range(11)]
+    r = oracle.blasst_rows(q, k, v, row_keys, 0, 203, block_c, 0.2, 0.0)
+    o_ref, lse_ref = _library_attention(q, k, v, row_keys, 0.2)
+    np.testing.assert_allclose(r["o"], o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], lse_ref, rtol=1e-12, atol=1e-12)
+    assert r["skipped"] == 0
+    assert r["visited"] == -(-203 // block_c)
+
+
+def _sdpa(q, k, v, causal):
+    """torch SDPA in float64 on [B, L, H, d] tensors (GQA by repeating KV heads)."""
+    qt = torch.as_tensor(q, dtype=torch.float64).transpose(1, 2)
+    kt = torch.as_tensor(k, dtype=torch.float64).transpose(1, 2)
+    vt = torch.as_tensor(v, dtype=torch.float64).transpose(1, 2)
+    grp = qt.shape[1] // kt.shape[1]
+    kt = kt.repeat_interleave(grp, dim=1)
+    vt = vt.repeat_interleave(grp, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal)
+    return o.transpose(1, 2).numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_lambda_zero_matches_torch_sdpa(causal):
+    from flashattention_softmax_threshold_amd.inputs import prefill_inputs
+
+    B, L, Hq, Hkv, d = 2, 150, 4, 2, 16
+    q, k, v = prefill_inputs(B=B, L=L, Hq=Hq, Hkv=Hkv, d=d, cluster_len=32, dtype=torch.float32,
+                             seed=3, beta=4.0, sinks=8)
+    res = oracle.prefill(q, k, v, causal=causal, block_r=32, block_c=16, scale=1 / math.sqrt(d),
+                         lam=0.0)
+    ref = _sdpa(q.numpy(), k.numpy(), v.numpy(), causal)
+    for (b, h, qb), u in res.units.items():
+        r0 = qb * 32
+        np.testing.assert_allclose(u.o, ref[b, r0:r0 + u.o.shape[0], h], rtol=1e-10, atol=1e-11)
+        assert u.skipped == 0
+    assert len(res.units) == B * Hq * (-(-L // 32))
+    # Visited tiles: all 10 (ragged last) non-causal; causal block qb sees tiles up to its last row.
+    for (b, h, qb), u in res.units.items():
+        last_row = min((qb + 1) * 32, L) - 1
+        expect = (last_row // 16 + 1) if causal else -(-L // 16)
+        assert u.visited == expect
+
+
+def test_decode_lambda_zero_matches_torch_sdpa_with_lengths_and_splits():
+    from flashattention_softmax_threshold_amd.inputs import decode_inputs
+
+    B, Hq, Hkv, L, d, dv = 3, 8, 2, 300, 16, 12
+    kv_len = [300, 1, 129]
+    q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=Hkv, L=L, d_qk=d, d_v=dv, cluster_len=50,
+                                 dtype=torch.float32, seed=5, beta=3.0, kv_len=kv_len)
+    for splits in (1, 2, 5):
+        res = oracle.decode(q, k, v, kv_len=kvl, block_r=4, block_c=32, num_splits=splits,
+                            scale=0.25, lam=0.0)
+        for (b, g, rb), u in res.units.items():
+            n = kv_len[b]
+            heads = range(g * 4 + rb * 4, g * 4 + rb * 4 + 4)
+            for i, h in enumerate(heads):
+                s = 0.25 * (k[b, :n, g].double() @ q[b, h].double())
+                ref = torch.softmax(s, 0) @ v[b, :n, g].double()
+                np.testing.assert_allclose(u.o[i], ref.numpy(), rtol=1e-11, atol=1e-12)
+                np.testing.assert_allclose(u.lse[i], torch.logsumexp(s, 0).item(), rtol=1e-12)
+
+
+def test_decode_empty_sequence_gives_zero_and_minus_inf():
+    q = np.ones((1, 2, 4))
+    k = np.ones((1, 10, 1, 4))
+    v = np.ones((1, 10, 1, 3))
+    for splits in (1, 3):
+        res = oracle.decode(q, k, v, kv_len=[0], block_r=2, block_c=4, num_splits=splits,
+                            scale=1.0, lam=0.1)
+        u = res.units[(0, 0, 0)]
+        assert np.all(u.o == 0) and np.all(np.isneginf(u.lse))
+        assert u.visited == 0 and u.skipped == 0
+
+
+# ------------------------------------------------------------------------------------------
+# lambda > 0: closed form, invariants, worked example
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(6))
+def test_streaming_matches_closed_form(seed):
+    rng = np.random.default_rng(100 + seed)
+    n_rows = int(rng.integers(1, 9))
+    n_keys = int(rng.integers(40, 400))
+    block_c = int(rng.choice([8, 16, 33]))
+    q, k, v = _clustered_rows(rng, n_rows, n_keys, 16, 6, beta=float(rng.choice([4.0, 8.0])))
+    row_keys = sorted(rng.integers(1, n_keys + 1, size=n_rows).tolist())
+    scale = 0.25
+    total_skips = 0
+    for lam in (0.0, 1e-4, 1e-2, 0.3, 1.0):
+        r = oracle.blasst_rows(q, k, v, row_keys, 0, n_keys, block_c, scale, lam)
+        cf = _closed_form(q, k, v, row_keys, scale, lam, block_c)
+        vis = cf["visited"]
+        np.testing.assert_array_equal(r["tile_status"][vis] == oracle.TILE_SKIPPED,
+                                      cf["skipped"][vis])
+        assert np.all(r["tile_status"][~vis] == oracle.TILE_NOT_VISITED)
+        np.testing.assert_allclose(r["tile_margin"][vis], cf["margin"][vis], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r["o"], cf["o"], rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(r["lse"], cf["lse"], rtol=1e-12, atol=1e-12)
+        assert r["visited"] == int(vis.sum())
+        assert r["skipped"] == int(cf["skipped"].sum())
+        total_skips += r["skipped"]
+    assert total_skips > 0  # the case exercises the skip branch
+
+
+def test_worked_example_from_golden_fixture():
+    fx = json.load(open(os.path.join(GOLDEN, "hand_tiles.json")))
+    k = np.array(fx["k"])
+    v = np.array(fx["v"])
+    for case in fx["cases"]:
+        q = np.array(case["rows"])
+        row_keys = case.get("row_keys", [len(k)] * len(q))
+        lam = 0.0 if case.get("lambda_zero") else math.exp(case["ln_lambda"])
+        r = oracle.blasst_rows(q, k, v, row_keys, 0, len(k), fx["block_c"], fx["scale"], lam)
+        assert r["tile_status"].tolist() == case["status"], case
+        np.testing.assert_allclose(r["tile_margin"], case["margin"], atol=1e-12)
+        # Output: plain softmax over the keys of the kept tiles, written out with math.exp.
+        kept = [j for j in range(len(k)) if case["status"][j // fx["block_c"]] == 0]
+        for i, row in enumerate(q):
+            ks = [j for j in kept if j < row_keys[i]]
+            w = [math.exp(row[0] * k[j][0]) for j in ks]
+            expect = [sum(wj * v[j][c] for wj, j in zip(w, ks)) / sum(w) for c in range(2)]
+            np.testing.assert_allclose(r["o"][i], expect, rtol=1e-13)
+            assert abs(r["lse"][i] - math.log(sum(w))) < 1e-13
+
+
+def test_margin_in_range_and_first_tile_kept():
+    rng = np.random.default_rng(7)
+    q, k, v = _clustered_rows(rng, 5, 333, 16, 4, beta=8.0)
+    r = oracle.blasst_rows(q, k, v, [333] * 5, 0, 333, 16, 0.25, 0.5)
+    m = r["tile_margin"]
+    assert np.all(m <= 0)  # exp(margin) lies in (0, 1]
+    assert np.all(np.exp(m) > 0)
+    assert m[0] == 0 and r["tile_status"][0] == oracle.TILE_KEPT
+
+
+def test_skipped_set_monotone_in_lambda_and_fixed_by_margin():
+    rng = np.random.default_rng(11)
+    q, k, v = _clustered_rows(rng, 4, 512, 16, 4, beta=8.0)
+    lams = [0.0, 1e-6, 1e-4, 1e-3, 1e-2, 0.1, 0.5, 1.0]
+    prev = None
+    margins = None
+    for lam in lams:
+        r = oracle.blasst_rows(q, k, v, [512] * 4, 0, 512, 32, 0.25, lam)
+        sk = r["tile_status"] == oracle.TILE_SKIPPED
+        if margins is None:
+            margins = r["tile_margin"]
+        np.testing.assert_array_equal(r["tile_margin"], margins)  # margin does not depend on lambda
+        tau = -np.inf if lam == 0 else math.log(lam)
+        np.testing.assert_array_equal(sk, margins < tau)
+        if prev is not None:
+            assert np.all(sk >= prev)
+        prev = sk
+    assert prev.sum() > 0
+
+
+def test_lambda_one_uses_strict_comparison_and_lambda_above_one_is_clamped():
+    # All keys identical: every tile margin is exactly 0, so "0 < ln(1) = 0" is false and nothing
+    # is skipped; a "<=" test would skip every tile after the first.
+    n = 70
+    q = np.ones((3, 4))
+    k = np.ones((n, 4))
+    v = np.arange(n, dtype=float)[:, None] * np.ones((1, 2))
+    for lam in (1.0, 7.5):
+        r = oracle.blasst_rows(q, k, v, [n] * 3, 0, n, 16, 1.0, lam)
+        assert r["skipped"] == 0
+        np.testing.assert_allclose(r["o"], np.full((3, 2), (n - 1) / 2.0), rtol=1e-14)
+    r1 = oracle.blasst_rows(*_clustered_rows(np.random.default_rng(1), 3, 200, 8, 2, 8.0),
+                            [200] * 3, 0, 200, 16, 0.3, 1.0)
+    r2 = oracle.blasst_rows(*_clustered_rows(np.random.default_rng(1), 3, 200, 8, 2, 8.0),
+                            [200] * 3, 0, 200, 16, 0.3, 40.0)
+    np.testing.assert_array_equal(r1["tile_status"], r2["tile_status"])
+    np.testing.assert_array_equal(r1["o"], r2["o"])
+
+
+@pytest.mark.parametrize("lam", [-1e-9, float("nan"), float("inf")])
+def test_invalid_lambda_rejected(lam):
+    with pytest.raises(oracle.OracleError):
+        oracle.blasst_rows(np.ones((1, 2)), np.ones((4, 2)), np.ones((4, 2)), [4], 0, 4, 2, 1.0, lam)
+
+
+def test_error_bounded_by_skipped_mass():
+    """|O_blasst - O_dense| <= 2 max|V| W / l_kept <= 2 max|V| W, with W the skipped weight
+    sum_{skipped k} exp(s_k - M) (M the global row max); each skipped weight is below lambda, the
+    Skip-Softmax page's upper-bound argument."""
+    rng = np.random.default_rng(21)
+    q, k, v = _clustered_rows(rng, 6, 640, 16, 5, beta=6.0)
+    row_keys = [640] * 6
+    o_dense, _ = _library_attention(q, k, v, row_keys, 0.25)
+    s = _masked_scores(q, k, row_keys, 0.25)
+    M = s.max(axis=1, keepdims=True)
+    checked = 0
+    for lam in (1e-4, 1e-3, 1e-2, 0.1, 0.5):
+        r = oracle.blasst_rows(q, k, v, row_keys, 0, 640, 32, 0.25, lam)
+        skip_cols = np.repeat(r["tile_status"] == oracle.TILE_SKIPPED, 32)[:640]
+        w = np.exp(s - M)
+        W = (w * skip_cols[None, :]).sum(axis=1)
+        l_kept = (w * ~skip_cols[None, :]).sum(axis=1)
+        err = np.abs(r["o"] - o_dense).max(axis=1)
+        vmax = np.abs(v).max()
+        assert np.all(err <= 2 * vmax * W / l_kept + 1e-12)
+        assert np.all(l_kept >= 1.0 - 1e-12)  # the tile holding a row's global max is kept
+        assert np.all((w * skip_cols[None, :]) < lam)  # every skipped weight is below lambda
+        checked += int(skip_cols.sum() > 0)
+    assert checked >= 3
+
+
+def test_split_ranges_and_combine():
+    """Splits restart the running state; merged by log-sum-exp they reproduce the unsplit dense
+    result at lambda = 0, and each non-empty split keeps its first tile."""
+    rng = np.random.default_rng(33)
+    q, k, v = _clustered_rows(rng, 4, 500, 16, 6, beta=8.0)
+    assert oracle.split_ranges(500, 500, 32, 4) == [(0, 128), (128, 256), (256, 384), (384, 500)]
+    assert oracle.split_ranges(100, 500, 32, 4) == [(0, 100), (100, 100), (100, 100), (100, 100)]
+    parts = [oracle.blasst_rows(q, k, v, [500] * 4, a, e, 32, 0.25, 0.0)
+             for a, e in oracle.split_ranges(500, 500, 32, 4)]
+    o, lse = oracle.combine(np.stack([p["o"] for p in parts]), np.stack([p["lse"] for p in parts]))
+    o_ref, lse_ref = _library_attention(q, k, v, [500] * 4, 0.25)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12)
+    for lam in (0.01, 0.5):
+        for a, e in oracle.split_ranges(500, 500, 32, 4):
+            p = oracle.blasst_rows(q, k, v, [500] * 4, a, e, 32, 0.25, lam)
+            assert p["tile_status"][0] == oracle.TILE_KEPT
+            cf = _closed_form(q, k, v, [500] * 4, 0.25, lam, 32, k_begin=a, k_end=e)
+            np.testing.assert_allclose(p["o"], cf["o"], rtol=1e-10, atol=1e-11)
+
+
+def test_decode_units_and_splits_follow_closed_form():
+    from flashattention_softmax_threshold_amd.inputs import decode_inputs
+
+    B, Hq, Hkv, L, d = 2, 8, 2, 512, 16
+    q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=Hkv, L=L, d_qk=d, d_v=d, cluster_len=64,
+                                 dtype=torch.float32, seed=9, beta=8.0, share=True,
+                                 kv_len=[512, 300])
+    any_skip = 0
+    for splits in (1, 3):
+        res = oracle.decode(q, k, v, kv_len=kvl, block_r=4, block_c=32, num_splits=splits,
+                            scale=0.25, lam=0.05)
+        for (b, g, rb), u in res.units.items():
+            n = int(kvl[b])
+            qq = q[b, g * 4:(g + 1) * 4].double().numpy()
+            kk = k[b, :n, g].double().numpy()
+            vv = v[b, :n, g].double().numpy()
+            os_, ls_ = [], []
+            for a, e in oracle.split_ranges(n, 512, 32, splits):
+                if a == e:
+                    continue
+                cf = _closed_form(qq, kk, vv, [n] * 4, 0.25, 0.05, 32, k_begin=a, k_end=e)
+                os_.append(cf["o"])
+                ls_.append(cf["lse"])
+                any_skip += int(cf["skipped"].sum())
+            w = np.exp(np.array(ls_) - np.max(ls_, axis=0))
+            o_ref = (w[:, :, None] * np.array(os_)).sum(0) / w.sum(0)[:, None]
+            np.testing.assert_allclose(u.o, o_ref, rtol=1e-10, atol=1e-11)
+    assert any_skip > 0
