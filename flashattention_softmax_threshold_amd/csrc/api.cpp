@@ -1,0 +1,303 @@
+// api.cpp -- host side of the C ABI in include/blasst.h: argument checks, threshold resolution,
+// launch planning and dispatch to the HIP kernels. Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "blasst.h"
+#include "internal.h"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+
+bool finite_nonneg(double x) { return isfinite(x) && x >= 0.0; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Base-2 threshold the kernels compare against: log2(min(lambda, 1)), -inf for lambda == 0.
+float tau_log2(double lambda) {
+  const double lam = lambda > 1.0 ? 1.0 : lambda;
+  return lam > 0.0 ? (float)log2(lam) : -INFINITY;
+}
+
+float scale_log2(float softmax_scale, int head_dim) {
+  const double s = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / sqrt((double)head_dim);
+  return (float)(s * kLog2e);
+}
+
+bool strides_ok(const int64_t *st, int n, int64_t mult) {
+  for (int i = 0; i < n; ++i)
+    if (st[i] < 0 || st[i] % mult != 0) return false;
+  return true;
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char *blasst_status_string(blasst_status status) {
+  switch (status) {
+    case BLASST_OK: return "BLASST_OK";
+    case BLASST_ERR_INVALID_ARG: return "BLASST_ERR_INVALID_ARG";
+    case BLASST_ERR_UNSUPPORTED: return "BLASST_ERR_UNSUPPORTED";
+    case BLASST_ERR_NO_CALIBRATION: return "BLASST_ERR_NO_CALIBRATION";
+    case BLASST_ERR_CONFLICT: return "BLASST_ERR_CONFLICT";
+    case BLASST_ERR_HIP: return "BLASST_ERR_HIP";
+    case BLASST_ERR_WORKSPACE: return "BLASST_ERR_WORKSPACE";
+  }
+  return "BLASST_UNKNOWN_STATUS";
+}
+
+// "Skip-Softmax" page, "From configuration to the kernel threshold": the kernel receives
+// threshold_scale_factor and divides it by the call's max_kv_len; a threshold t is passed as
+// t * max_kv_len (so lambda = t); a target sparsity s is passed as a * exp(b * s).
+blasst_status blasst_resolve_lambda(const blasst_lambda_spec *spec, int64_t max_kv_len,
+                                    double *lambda_out) {
+  if (!spec || !lambda_out) return BLASST_ERR_INVALID_ARG;
+  switch (spec->mode) {
+    case BLASST_DENSE:
+      *lambda_out = 0.0;
+      return BLASST_OK;
+    case BLASST_THRESHOLD:
+      if (!finite_nonneg(spec->threshold)) return BLASST_ERR_INVALID_ARG;
+      *lambda_out = spec->threshold;
+      return BLASST_OK;
+    case BLASST_SCALE_FACTOR: {
+      if (!finite_nonneg(spec->scale_factor) || max_kv_len <= 0) return BLASST_ERR_INVALID_ARG;
+      const double lam = spec->scale_factor / (double)max_kv_len;
+      if (!isfinite(lam)) return BLASST_ERR_INVALID_ARG;
+      *lambda_out = lam;
+      return BLASST_OK;
+    }
+    case BLASST_TARGET_SPARSITY: {
+      if (spec->threshold > 0.0 || spec->scale_factor > 0.0) return BLASST_ERR_CONFLICT;
+      const double s = spec->target_sparsity;
+      if (!(s >= 0.0 && s <= 1.0) || max_kv_len <= 0) return BLASST_ERR_INVALID_ARG;
+      if (!spec->has_calibration) return BLASST_ERR_NO_CALIBRATION;
+      if (!isfinite(spec->a) || !isfinite(spec->b) || spec->a < 0.0) return BLASST_ERR_INVALID_ARG;
+      const double lam = spec->a * exp(spec->b * s) / (double)max_kv_len;
+      if (!finite_nonneg(lam)) return BLASST_ERR_INVALID_ARG;
+      *lambda_out = lam;
+      return BLASST_OK;
+    }
+  }
+  return BLASST_ERR_INVALID_ARG;
+}
+
+// "Skip-Softmax" page, "Timestep gating": dense while t is above the cutoff; cutoff 0 is the
+// "gate off" sentinel; without a published t a positive cutoff keeps the call dense.
+blasst_status blasst_timestep_gate(double disabled_until_timestep, int32_t has_t, double t,
+                                   int32_t *active) {
+  if (!active || !(disabled_until_timestep >= 0.0) || !isfinite(disabled_until_timestep))
+    return BLASST_ERR_INVALID_ARG;
+  if (disabled_until_timestep == 0.0) {
+    *active = 1;
+    return BLASST_OK;
+  }
+  if (!has_t) {
+    *active = 0;
+    return BLASST_OK;
+  }
+  if (isnan(t)) return BLASST_ERR_INVALID_ARG;
+  *active = t <= disabled_until_timestep ? 1 : 0;
+  return BLASST_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// Prefill
+// ------------------------------------------------------------------------------------------
+blasst_status blasst_prefill_tiles(const blasst_prefill_args *a, int32_t *block_r,
+                                   int32_t *block_c) {
+  if (!a || !block_r || !block_c) return BLASST_ERR_INVALID_ARG;
+  if (a->dtype != BLASST_BF16 && a->dtype != BLASST_F32) return BLASST_ERR_UNSUPPORTED;
+  const int br = a->block_r ? a->block_r : (a->dtype == BLASST_BF16 ? 128 : 64);
+  const int bc = a->block_c ? a->block_c : blasst::kBlockC;
+  if (br != 32 && br != 64 && br != 128) return BLASST_ERR_UNSUPPORTED;
+  if (bc != blasst::kBlockC) return BLASST_ERR_UNSUPPORTED;
+  *block_r = br;
+  *block_c = bc;
+  return BLASST_OK;
+}
+
+blasst_status blasst_attn_prefill(const blasst_prefill_args *a, void *stream) {
+  if (!a) return BLASST_ERR_INVALID_ARG;
+  if (a->dtype != BLASST_BF16 && a->dtype != BLASST_F32) return BLASST_ERR_UNSUPPORTED;
+  if (a->batch < 0 || a->len_q < 0 || a->len_kv < 0 || a->heads_q <= 0 || a->heads_kv <= 0)
+    return BLASST_ERR_INVALID_ARG;
+  if (a->heads_q % a->heads_kv != 0) return BLASST_ERR_INVALID_ARG;
+  if (a->causal && a->len_q != a->len_kv) return BLASST_ERR_INVALID_ARG;
+  if (!finite_nonneg(a->lambda)) return BLASST_ERR_INVALID_ARG;
+  if (!(a->softmax_scale >= 0.f) || !isfinite(a->softmax_scale)) return BLASST_ERR_INVALID_ARG;
+  if (a->head_dim != 64 && a->head_dim != 128) return BLASST_ERR_UNSUPPORTED;
+  int32_t br, bc;
+  blasst_status st = blasst_prefill_tiles(a, &br, &bc);
+  if (st != BLASST_OK) return st;
+  if (a->batch == 0 || a->len_q == 0) return BLASST_OK;  // nothing to compute
+  if (a->len_kv == 0) return BLASST_ERR_INVALID_ARG;      // rows with no key at all
+  if (!a->q || !a->k || !a->v || !a->o) return BLASST_ERR_INVALID_ARG;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return BLASST_ERR_INVALID_ARG;
+  const int64_t mult = a->dtype == BLASST_BF16 ? 8 : 4;
+  if (!strides_ok(a->q_stride, 3, mult) || !strides_ok(a->k_stride, 3, mult) ||
+      !strides_ok(a->v_stride, 3, mult) || !strides_ok(a->o_stride, 3, mult))
+    return BLASST_ERR_INVALID_ARG;
+  const int n_qb = ceil_div(a->len_q, br);
+  if (a->heads_q > 65535 || a->batch > 65535) return BLASST_ERR_UNSUPPORTED;
+
+  blasst::PrefillParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o;
+  p.q_sb = a->q_stride[0]; p.q_ss = a->q_stride[1]; p.q_sh = a->q_stride[2];
+  p.k_sb = a->k_stride[0]; p.k_ss = a->k_stride[1]; p.k_sh = a->k_stride[2];
+  p.v_sb = a->v_stride[0]; p.v_ss = a->v_stride[1]; p.v_sh = a->v_stride[2];
+  p.o_sb = a->o_stride[0]; p.o_ss = a->o_stride[1]; p.o_sh = a->o_stride[2];
+  p.B = a->batch; p.Hq = a->heads_q; p.Hkv = a->heads_kv; p.Lq = a->len_q; p.Lkv = a->len_kv;
+  p.causal = a->causal ? 1 : 0;
+  p.n_qblocks = n_qb;
+  p.n_kvtiles = ceil_div(a->len_kv, bc);
+  p.scale_log2 = scale_log2(a->softmax_scale, a->head_dim);
+  p.tau_log2 = tau_log2(a->lambda);
+  p.lse = a->lse;
+  p.counters = a->counters;
+  p.tile_status = a->tile_status;
+  p.tile_margin = a->tile_margin;
+  const hipError_t err =
+      blasst::launch_prefill(p, a->dtype == BLASST_BF16 ? 1 : 0, a->head_dim, br,
+                             (hipStream_t)stream);
+  return err == hipSuccess ? BLASST_OK : BLASST_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode
+// ------------------------------------------------------------------------------------------
+namespace {
+
+enum DecodeKind { kNone = 0, kGqa = 1, kMla = 2 };
+
+DecodeKind decode_kind(const blasst_decode_args *a) {
+  if (a->dtype != BLASST_BF16) return kNone;
+  if (a->head_dim_qk == a->head_dim_v && (a->head_dim_qk == 128 || a->head_dim_qk == 64))
+    return kGqa;
+  if (a->head_dim_qk == 576 && a->head_dim_v == 512 && a->heads_kv == 1 && a->v == a->k)
+    return kMla;
+  return kNone;
+}
+
+// Split count chosen by the library: enough work units to give every CU about two of them,
+// but at least 8 tiles per split.
+int auto_splits(int units, int n_tiles) {
+  const int target = 2 * 256;
+  if (units >= target || n_tiles <= 8) return 1;
+  int s = ceil_div(target, units);
+  const int max_s = n_tiles / 8 > 0 ? n_tiles / 8 : 1;
+  if (s > max_s) s = max_s;
+  if (s > 64) s = 64;
+  return s < 1 ? 1 : s;
+}
+
+}  // namespace
+
+blasst_status blasst_decode_plan(const blasst_decode_args *a, int32_t *block_r, int32_t *block_c,
+                                 int32_t *num_splits) {
+  if (!a || !block_r || !block_c || !num_splits) return BLASST_ERR_INVALID_ARG;
+  if (a->heads_q <= 0 || a->heads_kv <= 0 || a->heads_q % a->heads_kv != 0 || a->batch < 0 ||
+      a->max_kv_len < 0)
+    return BLASST_ERR_INVALID_ARG;
+  const DecodeKind kind = decode_kind(a);
+  if (kind == kNone) return BLASST_ERR_UNSUPPORTED;
+  const int group = a->heads_q / a->heads_kv;
+  const int bc = a->block_c ? a->block_c : blasst::kBlockC;
+  if (bc != blasst::kBlockC) return BLASST_ERR_UNSUPPORTED;
+  int br;
+  if (kind == kGqa) {
+    br = a->block_r ? a->block_r : (group < 16 ? group : 16);
+    if (br < 1 || br > 16) return BLASST_ERR_UNSUPPORTED;
+  } else {
+    br = a->block_r ? a->block_r : 64;
+    if (br != 64 && br != 128) return BLASST_ERR_UNSUPPORTED;
+  }
+  if (br > group) br = group;
+  const int n_tiles = ceil_div(a->max_kv_len, bc);
+  int s = a->num_splits;
+  if (s < 0) return BLASST_ERR_INVALID_ARG;
+  if (s == 0) {
+    const int units = a->batch * a->heads_kv * ceil_div(group, br);
+    s = auto_splits(units > 0 ? units : 1, n_tiles);
+  }
+  if (s > 256) return BLASST_ERR_UNSUPPORTED;
+  *block_r = br;
+  *block_c = bc;
+  *num_splits = s;
+  return BLASST_OK;
+}
+
+size_t blasst_decode_workspace_size(const blasst_decode_args *a) {
+  int32_t br, bc, s;
+  if (blasst_decode_plan(a, &br, &bc, &s) != BLASST_OK || s <= 1) return 0;
+  const size_t rows = (size_t)a->batch * (size_t)a->heads_q * (size_t)s;
+  const size_t o_bytes = rows * (size_t)a->head_dim_v * sizeof(float);
+  const size_t l_bytes = rows * sizeof(float);
+  return ((o_bytes + 255) / 256) * 256 + ((l_bytes + 255) / 256) * 256;
+}
+
+blasst_status blasst_attn_decode(const blasst_decode_args *a, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+  if (!a) return BLASST_ERR_INVALID_ARG;
+  if (!finite_nonneg(a->lambda)) return BLASST_ERR_INVALID_ARG;
+  if (!(a->softmax_scale >= 0.f) || !isfinite(a->softmax_scale)) return BLASST_ERR_INVALID_ARG;
+  int32_t br, bc, s;
+  blasst_status st = blasst_decode_plan(a, &br, &bc, &s);
+  if (st != BLASST_OK) return st;
+  if (a->batch == 0) return BLASST_OK;
+  if (!a->q || !a->k || !a->v || !a->o) return BLASST_ERR_INVALID_ARG;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return BLASST_ERR_INVALID_ARG;
+  if (!strides_ok(a->q_stride, 2, 8) || !strides_ok(a->k_stride, 3, 8) ||
+      !strides_ok(a->v_stride, 3, 8) || !strides_ok(a->o_stride, 2, 8))
+    return BLASST_ERR_INVALID_ARG;
+  if (a->batch > 65535 || a->heads_kv > 65535) return BLASST_ERR_UNSUPPORTED;
+  const size_t need = blasst_decode_workspace_size(a);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)))
+    return BLASST_ERR_WORKSPACE;
+
+  const DecodeKind kind = decode_kind(a);
+  blasst::DecodeParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o;
+  p.q_sb = a->q_stride[0]; p.q_sh = a->q_stride[1];
+  p.k_sb = a->k_stride[0]; p.k_ss = a->k_stride[1]; p.k_sh = a->k_stride[2];
+  p.v_sb = a->v_stride[0]; p.v_ss = a->v_stride[1]; p.v_sh = a->v_stride[2];
+  p.o_sb = a->o_stride[0]; p.o_sh = a->o_stride[1];
+  p.kv_len = a->kv_len;
+  p.B = a->batch; p.Hq = a->heads_q; p.Hkv = a->heads_kv; p.max_kv_len = a->max_kv_len;
+  p.group = a->heads_q / a->heads_kv;
+  p.block_r = br;
+  p.n_rblocks = ceil_div(p.group, br);
+  p.n_tiles = ceil_div(a->max_kv_len, bc);
+  p.num_splits = s;
+  p.tiles_per_split = p.n_tiles > 0 ? ceil_div(p.n_tiles, s) : 0;
+  p.scale_log2 = scale_log2(a->softmax_scale, a->head_dim_qk);
+  p.tau_log2 = tau_log2(a->lambda);
+  p.lse = a->lse;
+  p.counters = a->counters;
+  p.tile_status = a->tile_status;
+  p.tile_margin = a->tile_margin;
+  if (s > 1) {
+    const size_t rows = (size_t)a->batch * (size_t)a->heads_q * (size_t)s;
+    const size_t o_bytes = ((rows * (size_t)a->head_dim_v * sizeof(float) + 255) / 256) * 256;
+    p.o_part = (float *)workspace;
+    p.lse_part = (float *)((char *)workspace + o_bytes);
+  }
+  hipError_t err;
+  if (kind == kGqa) {
+    err = blasst::launch_decode_gqa(p, a->head_dim_qk, (hipStream_t)stream);
+  } else {
+    err = blasst::launch_decode_mla(p, (hipStream_t)stream);
+  }
+  if (err == hipSuccess && s > 1)
+    err = blasst::launch_split_combine(p, a->head_dim_v, (hipStream_t)stream);
+  return err == hipSuccess ? BLASST_OK : BLASST_ERR_HIP;
+}
+
+}  // extern "C"

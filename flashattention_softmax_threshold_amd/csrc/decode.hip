@@ -1,0 +1,347 @@
+// decode.hip -- BLASST skip-softmax decode for GQA / MQA on gfx950, and the split merge.
+//
+// Method: "Skip-Softmax" (vLLM-Omni design page), "Algorithm" (per-tile test on
+// tile_max - running_max < ln lambda over every query row of the tile). Decode follows the
+// BLASST talk notes ("kernel design: decode"): decode is bound by reading the KV cache, so a
+// skipped tile must not load its V tile at all; the K tiles of a batch are loaded back to back,
+// the test is taken for all of them, and only the surviving V tiles are requested.
+//
+// Work unit (one workgroup, 4 waves): (split, KV head g, block of up to RB query heads that share
+// g, sequence b); the rows of a tile are those query heads. A "round" is 4 consecutive key tiles,
+// one per wave:
+//   1. each wave computes S^T = K Q^T for its tile with v_mfma_f32_16x16x32_bf16, the K fragments
+//      coming straight from HBM into registers (no LDS); then it requests the K tile of the next
+//      round, so K stays in flight while this round finishes;
+//   2. tile row maxima meet in LDS; every wave forms the same running (prefix) maxima over the 4
+//      tiles in key order, the same per-tile votes and the round maximum M;
+//   3. a wave whose tile is kept requests its V tile only now, writes P = exp2(S - M) to LDS and
+//      accumulates O += P V on the vector ALUs (16-byte V loads, one 8-column slice per lane);
+//      skipped tiles load no V at all;
+//   4. at the end the 4 waves' partial O and l are summed through LDS.
+// Using the round maximum M for P (instead of re-scaling tile by tile) is the same online
+// softmax in exact arithmetic; the skip decisions use each tile's own prefix maximum.
+#include "internal.h"
+
+#include <math.h>
+
+namespace blasst {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 &u, float *f) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <int D, int RB>
+__global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
+  constexpr int STEPS = D / 32;  // k-steps of one 16x16x32 MFMA chain
+  constexpr int CPR = D / 8;     // 16-byte chunks per key row
+  constexpr int KPI = 64 / CPR;  // keys covered by one V load instruction
+  constexpr int VL = 64 / KPI;   // V loads per lane per tile
+  __shared__ float sT[2][4][16];
+  __shared__ __attribute__((aligned(16))) float sP[4][64][RB];
+  __shared__ __attribute__((aligned(16))) float sO[4][RB][D];
+  __shared__ float sL[4][16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int n = lane & 15;     // S^T column = query row
+  const int kgrp = lane >> 4;  // which 8 of the 32 k values / which 4 keys of a 16-key block
+  const int split = blockIdx.x;
+  const int g = blockIdx.y / p.n_rblocks;
+  const int rb = blockIdx.y % p.n_rblocks;
+  const int b = blockIdx.z;
+  const int h0 = g * p.group + rb * p.block_r;
+  const int nrows = min(p.block_r, p.group - rb * p.block_r);
+  int seq_len = p.kv_len ? p.kv_len[b] : p.max_kv_len;
+  seq_len = max(0, min(seq_len, p.max_kv_len));
+  const int seq_tiles = (seq_len + kBlockC - 1) / kBlockC;
+  const int t_begin = split * p.tiles_per_split;
+  const int t_split_end = min(t_begin + p.tiles_per_split, p.n_tiles);
+  const int t_end = min(t_split_end, seq_tiles);
+
+  const __bf16 *__restrict__ Kg = (const __bf16 *)p.k + b * p.k_sb + g * p.k_sh;
+  const __bf16 *__restrict__ Vg = (const __bf16 *)p.v + b * p.v_sb + g * p.v_sh;
+  const int64_t unit_tiles =
+      (((int64_t)b * p.Hkv + g) * p.n_rblocks + rb) * (int64_t)p.n_tiles;
+
+  // Q fragments: B operand (k = head dim, n = query row); rows past nrows are zero.
+  bf16x8_t qf[STEPS];
+  {
+    const bool ok = n < nrows;
+    const __bf16 *qrow = (const __bf16 *)p.q + b * p.q_sb + (int64_t)(h0 + (ok ? n : 0)) * p.q_sh;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+      qf[s] = ok ? *(const bf16x8_t *)(qrow + 32 * s + 8 * kgrp) : (bf16x8_t)(__bf16)0.f;
+  }
+
+  bf16x8_t kreg[4 * STEPS];
+  auto load_k = [&](int t) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = t * kBlockC + 16 * kb + n;
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s)
+        kreg[kb * STEPS + s] = key < seq_len
+                                   ? *(const bf16x8_t *)(Kg + (int64_t)key * p.k_ss + 32 * s + 8 * kgrp)
+                                   : (bf16x8_t)(__bf16)0.f;
+    }
+  };
+
+  float o[RB][8];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+  float l_part = 0.f;
+  float m_run = -INFINITY;
+  unsigned visited = 0, skipped = 0;
+  const int n_rounds = t_end > t_begin ? (t_end - t_begin + 3) / 4 : 0;
+  const int vc = lane % CPR;   // V column chunk of this lane
+  const int vk = lane / CPR;   // V key offset of this lane inside a load instruction
+
+  if (n_rounds > 0 && t_begin + wv < t_end) load_k(t_begin + wv);
+
+  for (int r = 0; r < n_rounds; ++r) {
+    const int t = t_begin + 4 * r + wv;
+    const bool have = t < t_end;
+    f32x4_t sacc[4];
+    float mt = -INFINITY;
+    if (have) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        sacc[kb] = (f32x4_t)0.f;
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[kb * STEPS + s], qf[s], sacc[kb],
+                                                              0, 0, 0);
+      }
+      if ((t + 1) * kBlockC > seq_len) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t * kBlockC + 16 * kb + 4 * kgrp + i >= seq_len) sacc[kb][i] = -INFINITY;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sacc[kb][i]);
+      if (t + 4 < t_end) load_k(t + 4);  // next round's K, in flight during this round
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) sacc[kb] = (f32x4_t)0.f;
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mt2 = (n < nrows) ? mt * p.scale_log2 : -INFINITY;
+    if (lane < 16) sT[r & 1][wv][lane] = mt2;
+    __syncthreads();
+
+    // Prefix running maxima over the round's 4 tiles (key order) and the votes.
+    float mp = m_run;
+    bool keep_w[4];
+    float dmy = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float tm = sT[r & 1][w][n];
+      const float m2 = fmaxf(mp, tm);
+      const float dl = tm - m2;
+      const bool valid = (n < nrows) && tm > -INFINITY;
+      keep_w[w] = __ballot(valid && !(dl < p.tau_log2)) != 0ull;
+      if (w == wv) dmy = valid ? dl : -INFINITY;
+      mp = m2;
+    }
+    const float M = mp;
+    const bool my_keep = have && keep_w[wv];
+
+    // V tile only for a kept tile.
+    uint4 vreg[VL];
+    if (my_keep) {
+#pragma unroll
+      for (int kk = 0; kk < VL; ++kk) {
+        const int key = t * kBlockC + kk * KPI + vk;
+        vreg[kk] = key < seq_len ? *(const uint4 *)(Vg + (int64_t)key * p.v_ss + 8 * vc)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    const float alpha = exp2_fast(m_run - M_use);
+    l_part *= alpha;
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[rr][e] *= alpha;
+
+    if (my_keep) {
+      float ps = 0.f;
+      const bool row_live = n < nrows;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = row_live ? exp2_fast(fmaf(sacc[kb][i], p.scale_log2, -M_use)) : 0.f;
+          ps += pv;
+          if (n < RB) sP[wv][16 * kb + 4 * kgrp + i][n] = pv;
+        }
+      }
+      l_part += ps;
+      wave_lds_sync();
+#pragma unroll
+      for (int kk = 0; kk < VL; ++kk) {
+        const int kl = kk * KPI + vk;
+        float pr[RB];
+#pragma unroll
+        for (int q4 = 0; q4 < RB / 4; ++q4) {
+          const float4 x = *(const float4 *)(&sP[wv][kl][4 * q4]);
+          pr[4 * q4 + 0] = x.x;
+          pr[4 * q4 + 1] = x.y;
+          pr[4 * q4 + 2] = x.z;
+          pr[4 * q4 + 3] = x.w;
+        }
+        float vf[8];
+        bf16x8_to_f32(vreg[kk], vf);
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[rr][e] = fmaf(pr[rr], vf[e], o[rr][e]);
+      }
+      wave_lds_sync();
+    }
+    m_run = M;
+
+    if (have) {
+      ++visited;
+      skipped += my_keep ? 0u : 1u;
+      if (p.tile_margin) {
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) dmy = fmaxf(dmy, __shfl_xor(dmy, off));
+      }
+      if (lane == 0) {
+        if (p.tile_status) p.tile_status[unit_tiles + t] = my_keep ? 0 : 1;
+        if (p.tile_margin) p.tile_margin[unit_tiles + t] = dmy * kLn2;
+      }
+    }
+  }
+
+  // ---- Sum the waves' partials; write O (unsplit) or the split's partial.
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = o[rr][e];
+#pragma unroll
+      for (int off = CPR; off < 64; off <<= 1) v += __shfl_xor(v, off);
+      o[rr][e] = v;
+    }
+  }
+  if (lane < CPR) {
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sO[wv][rr][8 * lane + e] = o[rr][e];
+  }
+  float lrow = l_part;
+  lrow += __shfl_xor(lrow, 16);
+  lrow += __shfl_xor(lrow, 32);
+  if (lane < 16) sL[wv][lane] = lrow;
+  __syncthreads();
+
+  for (int idx = tid; idx < nrows * D; idx += 256) {
+    const int rr = idx / D, d = idx % D;
+    const float L = sL[0][rr] + sL[1][rr] + sL[2][rr] + sL[3][rr];
+    const float acc = sO[0][rr][d] + sO[1][rr][d] + sO[2][rr][d] + sO[3][rr][d];
+    const float val = L > 0.f ? acc / L : 0.f;
+    const int h = h0 + rr;
+    if (p.num_splits == 1) {
+      ((__bf16 *)p.o)[b * p.o_sb + (int64_t)h * p.o_sh + d] = (__bf16)val;
+      if (d == 0 && p.lse)
+        p.lse[(int64_t)b * p.Hq + h] = L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t row = ((int64_t)b * p.Hq + h) * p.num_splits + split;
+      p.o_part[row * D + d] = val;
+      if (d == 0) p.lse_part[row] = L > 0.f ? m_run + __log2f(L) : -INFINITY;
+    }
+  }
+  if (lane == 0 && p.counters && visited) {
+    atomicAdd(&p.counters[0], (unsigned long long)visited);
+    atomicAdd(&p.counters[1], (unsigned long long)skipped);
+  }
+  if (tid == 0 && (p.tile_status || p.tile_margin)) {
+    for (int t = max(t_begin, t_end); t < t_split_end; ++t) {
+      if (p.tile_status) p.tile_status[unit_tiles + t] = 2;
+      if (p.tile_margin) p.tile_margin[unit_tiles + t] = -INFINITY;
+    }
+  }
+}
+
+// Merge of split partials by log-sum-exp ("The Hitchhiker's Guide", LSE output L = m + log l:
+// exp(L_s) is split s's softmax denominator). lse_part is in base-2 units.
+__global__ __launch_bounds__(128) void split_combine_kernel(DecodeParams p, int dv) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int S = p.num_splits;
+  const int64_t row0 = ((int64_t)b * p.Hq + h) * S;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, p.lse_part[row0 + s]);
+  float wsum = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float x = p.lse_part[row0 + s];
+    if (x > -INFINITY) wsum += exp2_fast(x - M);
+  }
+  for (int d = threadIdx.x; d < dv; d += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float x = p.lse_part[row0 + s];
+      if (x > -INFINITY) acc = fmaf(exp2_fast(x - M), p.o_part[(row0 + s) * dv + d], acc);
+    }
+    ((__bf16 *)p.o)[b * p.o_sb + (int64_t)h * p.o_sh + d] =
+        (__bf16)(M > -INFINITY ? acc / wsum : 0.f);
+  }
+  if (threadIdx.x == 0 && p.lse)
+    p.lse[(int64_t)b * p.Hq + h] = M > -INFINITY ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+hipError_t launch_gqa_d(const DecodeParams &p, hipStream_t stream) {
+  const dim3 grid(p.num_splits, p.Hkv * p.n_rblocks, p.B);
+  if (p.block_r <= 4)
+    hipLaunchKernelGGL((decode_gqa_kernel<D, 4>), grid, dim3(256), 0, stream, p);
+  else if (p.block_r <= 8)
+    hipLaunchKernelGGL((decode_gqa_kernel<D, 8>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_gqa_kernel<D, 16>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_gqa(const DecodeParams &p, int head_dim, hipStream_t stream) {
+  if (head_dim == 128) return launch_gqa_d<128>(p, stream);
+  if (head_dim == 64) return launch_gqa_d<64>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_combine(const DecodeParams &p, int head_dim_v, hipStream_t stream) {
+  hipLaunchKernelGGL(split_combine_kernel, dim3(p.Hq, p.B), dim3(128), 0, stream, p, head_dim_v);
+  return hipGetLastError();
+}
+
+}  // namespace blasst

@@ -1,0 +1,65 @@
+// internal.h -- launch parameters shared by the host entry points and the HIP kernels.
+// Not part of the public ABI (include/blasst.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace blasst {
+
+// Key tile width of every kernel here (B_c).
+constexpr int kBlockC = 64;
+
+struct PrefillParams {
+  const void *q, *k, *v;
+  void *o;
+  int64_t q_sb, q_ss, q_sh;  // strides in elements: batch, seq, head
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int B, Hq, Hkv, Lq, Lkv;
+  int causal;
+  int n_qblocks, n_kvtiles;
+  float scale_log2;  // softmax scale * log2(e): scores are kept in base-2 units
+  float tau_log2;    // log2(min(lambda, 1)), -inf for lambda == 0
+  float *lse;
+  unsigned long long *counters;
+  uint8_t *tile_status;
+  float *tile_margin;
+};
+
+// dtype: 0 fp32, 1 bf16. Returns hipSuccess or the launch error.
+hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_dim, int block_r,
+                          hipStream_t stream);
+
+struct DecodeParams {
+  const void *q, *k, *v;
+  void *o;
+  int64_t q_sb, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_sh;
+  const int32_t *kv_len;  // may be null: every sequence has max_kv_len keys
+  int B, Hq, Hkv, max_kv_len;
+  int group;           // Hq / Hkv
+  int block_r;         // query heads per unit
+  int n_rblocks;       // ceil(group / block_r)
+  int num_splits;
+  int tiles_per_split;
+  int n_tiles;         // ceil(max_kv_len / B_c)
+  float scale_log2;
+  float tau_log2;
+  float *lse;
+  unsigned long long *counters;
+  uint8_t *tile_status;
+  float *tile_margin;
+  // split partials (num_splits > 1): o_part [B, Hq, S, d_v] fp32, lse_part [B, Hq, S] (log2 units)
+  float *o_part;
+  float *lse_part;
+};
+
+hipError_t launch_decode_gqa(const DecodeParams &p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_mla(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_split_combine(const DecodeParams &p, int head_dim_v, hipStream_t stream);
+
+}  // namespace blasst

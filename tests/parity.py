@@ -1,0 +1,71 @@
+"""Shared comparison rules for GPU-vs-oracle parity tests.
+
+Bar (bf16 inputs, fp32 accumulation): max|dO| <= 1e-2 * max|O| and mean|dO| <= 1e-3 over the
+compared outputs; LSE within 1e-2 (natural log). fp32 inputs: max|dO| <= 1e-4 * max|O|,
+mean|dO| <= 1e-5, LSE within 1e-4. Skip decisions must agree exactly on every tile whose oracle
+margin lies at least 1e-3 away from ln(lambda); inside that band float rounding may flip the
+decision, and such tiles are counted, not failed.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+MARGIN_BAND = 1e-3
+TOL = {
+    torch.bfloat16: dict(max_rel=1e-2, mean_abs=1e-3, lse_abs=1e-2),
+    torch.float32: dict(max_rel=1e-4, mean_abs=1e-5, lse_abs=1e-4),
+}
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def tau(lam: float) -> float:
+    return -math.inf if lam == 0 else math.log(min(lam, 1.0))
+
+
+def assert_outputs_close(o_gpu: np.ndarray, o_ref: np.ndarray, dtype, what: str):
+    tol = TOL[dtype]
+    err = np.abs(o_gpu - o_ref)
+    scale = np.abs(o_ref).max()
+    assert np.isfinite(o_gpu).all(), f"{what}: non-finite output"
+    assert err.max() <= tol["max_rel"] * scale, \
+        f"{what}: max|dO| {err.max():.3e} > {tol['max_rel']} * max|O| ({scale:.3e})"
+    assert err.mean() <= tol["mean_abs"], f"{what}: mean|dO| {err.mean():.3e}"
+    return float(err.max()), float(err.mean())
+
+
+def assert_lse_close(lse_gpu: np.ndarray, lse_ref: np.ndarray, dtype, what: str):
+    tol = TOL[dtype]["lse_abs"]
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse_gpu), fin), f"{what}: LSE finiteness differs"
+    if fin.any():
+        d = np.abs(lse_gpu[fin] - lse_ref[fin]).max()
+        assert d <= tol, f"{what}: LSE differs by {d:.3e}"
+
+
+def compare_tile_status(st_gpu: np.ndarray, st_ref: np.ndarray, margin_ref: np.ndarray,
+                        lam: float, what: str):
+    """Exact agreement outside the margin band; returns (#mismatches inside the band, #band)."""
+    st_gpu = np.asarray(st_gpu).ravel()
+    st_ref = np.asarray(st_ref).ravel()
+    margin_ref = np.asarray(margin_ref).ravel()
+    t = tau(lam)
+    band = np.isfinite(margin_ref) & (np.abs(margin_ref - t) < MARGIN_BAND) if math.isfinite(t) \
+        else np.zeros_like(st_ref, dtype=bool)
+    mism = st_gpu != st_ref
+    bad = mism & ~band
+    assert not bad.any(), f"{what}: {int(bad.sum())} tile decisions differ outside the band " \
+                          f"(first at {int(np.argmax(bad))}: gpu {st_gpu[bad][0]} ref {st_ref[bad][0]})"
+    return int(mism.sum()), int(band.sum())
+
+
+def oracle_scale(head_dim: int) -> float:
+    """1/sqrt(d): the library's default softmax scale."""
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,209 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports every entry point
+the public header declares, the threshold resolution and the timestep gate match the values the
+Skip-Softmax page prints, launch planning resolves its defaults, and bad arguments are refused
+before anything is launched."""
+import ctypes
+import json
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import flashattention_softmax_threshold_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "blasst.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(blasst_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    declared = _declared_functions()
+    assert set(declared) == set(F.EXPORTED)
+    lib = ctypes.CDLL(F.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(7):
+        assert F.blasst_status_string(code).startswith("BLASST_")
+
+
+def test_resolve_lambda_modes():
+    # Threshold: lambda itself, independent of the length.
+    assert F.blasst_resolve_lambda(F.BLASST_THRESHOLD, 4096, threshold=1e-3) == 1e-3
+    assert F.blasst_resolve_lambda(F.BLASST_THRESHOLD, 75600, threshold=1e-3) == 1e-3
+    assert F.blasst_resolve_lambda(F.BLASST_THRESHOLD, 10, threshold=0.0) == 0.0
+    # Scale factor: divided by the call's max_kv_len (lambda = a / L).
+    assert F.blasst_resolve_lambda(F.BLASST_SCALE_FACTOR, 8192, scale_factor=16.0) == 16.0 / 8192
+    assert F.blasst_resolve_lambda(F.BLASST_DENSE, 8192) == 0.0
+
+
+def test_resolve_lambda_target_sparsity_wan_calibration():
+    fx = json.load(open(os.path.join(GOLDEN, "wan22_calibration.json")))
+    a, b = fx["a"], fx["b"]
+    for s, L in ((fx["target_sparsity"], 75600), (0.5, 75600), (0.0, 1024), (1.0, 65536)):
+        lam = F.blasst_resolve_lambda(F.BLASST_TARGET_SPARSITY, L, target_sparsity=s, a=a, b=b)
+        assert lam == pytest.approx(a * math.exp(b * s) / L, rel=1e-15)
+    # The two operating points of the video-DiT workload.
+    assert F.blasst_resolve_lambda(F.BLASST_TARGET_SPARSITY, 75600, target_sparsity=0.5, a=a,
+                                   b=b) == pytest.approx(0.334986486358622, rel=1e-13)
+    assert F.blasst_resolve_lambda(F.BLASST_TARGET_SPARSITY, 75600, target_sparsity=0.7, a=a,
+                                   b=b) == pytest.approx(0.805723246153606, rel=1e-13)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mode=F.BLASST_THRESHOLD, threshold=-1e-3), F.BLASST_ERR_INVALID_ARG),
+    (dict(mode=F.BLASST_THRESHOLD, threshold=float("nan")), F.BLASST_ERR_INVALID_ARG),
+    (dict(mode=F.BLASST_THRESHOLD, threshold=float("inf")), F.BLASST_ERR_INVALID_ARG),
+    (dict(mode=F.BLASST_SCALE_FACTOR, scale_factor=4.0, L=0), F.BLASST_ERR_INVALID_ARG),
+    (dict(mode=F.BLASST_SCALE_FACTOR, scale_factor=-4.0), F.BLASST_ERR_INVALID_ARG),
+    (dict(mode=F.BLASST_TARGET_SPARSITY, target_sparsity=0.5), F.BLASST_ERR_NO_CALIBRATION),
+    (dict(mode=F.BLASST_TARGET_SPARSITY, target_sparsity=1.5, a=1.0, b=1.0), F.BLASST_ERR_INVALID_ARG),
+    (dict(mode=F.BLASST_TARGET_SPARSITY, target_sparsity=0.5, threshold=0.1, a=1.0, b=1.0),
+     F.BLASST_ERR_CONFLICT),
+    (dict(mode=7), F.BLASST_ERR_INVALID_ARG),
+])
+def test_resolve_lambda_errors(kw, code):
+    kw = dict(kw)
+    mode = kw.pop("mode")
+    L = kw.pop("L", 1000)
+    with pytest.raises(F.BlasstError) as e:
+        F.blasst_resolve_lambda(mode, L, **kw)
+    assert e.value.status == code
+
+
+def _minimax_schedule(shift, n):
+    us = [1.0 - i / n for i in range(n + 1)]
+    return [shift * u / (1 + (shift - 1) * u) for u in us][:n]
+
+
+def test_timestep_gate_reproduces_minimax_table():
+    fx = json.load(open(os.path.join(GOLDEN, "minimax_timestep_table.json")))
+    ts = _minimax_schedule(fx["shift"], fx["num_inference_steps"])
+    assert [round(t, 3) for t in ts[:5]] == fx["first_values"]
+    assert sum(t > 0.9 for t in ts) == fx["steps_above_0_9"]
+    for row in fx["rows"]:
+        active = [F.blasst_timestep_gate(row["disabled_until_timestep"], t) for t in ts]
+        assert active.count(False) == row["dense_steps"], row
+        assert active.count(True) == row["skip_softmax_steps"], row
+        # Once active, stays active (t only decreases).
+        first = active.index(True) if True in active else len(active)
+        assert all(active[first:])
+
+
+def test_timestep_gate_sentinel_and_unpublished_t():
+    assert F.blasst_timestep_gate(0.0, None) is True      # gate off: t is never read
+    assert F.blasst_timestep_gate(0.0, 0.999) is True
+    assert F.blasst_timestep_gate(1.0, None) is False     # positive cutoff, no t: dense
+    assert F.blasst_timestep_gate(1.0, 1.0) is True       # cutoff 1.0 with t: no dense step
+    with pytest.raises(F.BlasstError):
+        F.blasst_timestep_gate(-0.5, 0.3)
+    with pytest.raises(F.BlasstError):
+        F.blasst_timestep_gate(0.5, float("nan"))
+
+
+def _meta(shape, dtype=torch.bfloat16):
+    return torch.empty(shape, dtype=dtype, device="meta")
+
+
+def test_prefill_tile_defaults_and_unsupported():
+    q, k = _meta((1, 100, 8, 128)), _meta((1, 100, 2, 128))
+    assert F.blasst_prefill_tiles(q, k) == (128, 64)
+    assert F.blasst_prefill_tiles(q, k, block_r=64) == (64, 64)
+    q32, k32 = _meta((1, 100, 2, 64), torch.float32), _meta((1, 100, 2, 64), torch.float32)
+    assert F.blasst_prefill_tiles(q32, k32) == (64, 64)
+    for br, bc in ((96, 64), (128, 128)):
+        with pytest.raises(F.BlasstError) as e:
+            F.blasst_prefill_tiles(q, k, block_r=br, block_c=bc)
+        assert e.value.status == F.BLASST_ERR_UNSUPPORTED
+
+
+def test_decode_plan_defaults():
+    q, k = _meta((64, 32, 128)), _meta((64, 32768, 8, 128))
+    assert F.blasst_decode_plan(q, k, k) == (4, 64, 1)  # 512 units: no split needed
+    assert F.blasst_decode_workspace_size(q, k, k) == 0
+    q1, k1 = _meta((2, 32, 128)), _meta((2, 32768, 8, 128))
+    br, bc, s = F.blasst_decode_plan(q1, k1, k1)
+    assert (br, bc) == (4, 64) and s > 1
+    assert F.blasst_decode_workspace_size(q1, k1, k1) >= 2 * 32 * s * 129 * 4
+    # MQA: 32 query heads on one KV head -> blocks of 16 rows.
+    qm, km = _meta((4, 32, 128)), _meta((4, 1000, 1, 128))
+    assert F.blasst_decode_plan(qm, km, km)[0] == 16
+    with pytest.raises(F.BlasstError) as e:
+        F.blasst_decode_plan(_meta((4, 32, 96)), _meta((4, 1000, 1, 96)), _meta((4, 1000, 1, 96)))
+    assert e.value.status == F.BLASST_ERR_UNSUPPORTED
+
+
+def _prefill_struct(**over):
+    a = F._PrefillArgs()
+    a.dtype = F.BLASST_BF16
+    a.batch, a.heads_q, a.heads_kv, a.len_q, a.len_kv, a.head_dim = 1, 4, 2, 100, 100, 128
+    a.q = a.k = a.v = a.o = 1 << 20
+    for name in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        getattr(a, name)[:] = [100 * 4 * 128, 4 * 128, 128]
+    a.lam = 0.01
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(heads_kv=3), F.BLASST_ERR_INVALID_ARG),
+    (dict(causal=1, len_kv=50), F.BLASST_ERR_INVALID_ARG),
+    (dict(lam=-0.1), F.BLASST_ERR_INVALID_ARG),
+    (dict(lam=float("nan")), F.BLASST_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("inf")), F.BLASST_ERR_INVALID_ARG),
+    (dict(head_dim=96), F.BLASST_ERR_UNSUPPORTED),
+    (dict(q=0), F.BLASST_ERR_INVALID_ARG),
+    (dict(o=(1 << 20) + 8), F.BLASST_ERR_INVALID_ARG),
+    (dict(len_kv=0), F.BLASST_ERR_INVALID_ARG),
+    (dict(dtype=5), F.BLASST_ERR_UNSUPPORTED),
+])
+def test_prefill_rejects_bad_arguments_before_launch(over, code):
+    a = _prefill_struct(**over)
+    assert F.load_library().blasst_attn_prefill(ctypes.byref(a), None) == code
+
+
+def test_prefill_rejects_misaligned_stride():
+    a = _prefill_struct()
+    a.k_stride[1] = 4 * 128 + 3
+    assert F.load_library().blasst_attn_prefill(ctypes.byref(a), None) == F.BLASST_ERR_INVALID_ARG
+
+
+def test_prefill_empty_inputs_are_a_no_op():
+    for over in (dict(batch=0), dict(len_q=0, len_kv=0, causal=0)):
+        a = _prefill_struct(**over)
+        if "len_kv" in over:
+            a.len_kv = 0
+            a.len_q = 0
+        assert F.load_library().blasst_attn_prefill(ctypes.byref(a), None) == F.BLASST_OK
+
+
+def test_decode_rejects_bad_arguments_before_launch():
+    lib = F.load_library()
+    a = F._DecodeArgs()
+    a.dtype = F.BLASST_BF16
+    a.batch, a.heads_q, a.heads_kv, a.max_kv_len, a.head_dim_qk, a.head_dim_v = 2, 8, 2, 300, 128, 128
+    a.q = a.k = a.v = a.o = 1 << 20
+    a.q_stride[:] = [8 * 128, 128]
+    a.k_stride[:] = [300 * 2 * 128, 2 * 128, 128]
+    a.v_stride[:] = [300 * 2 * 128, 2 * 128, 128]
+    a.o_stride[:] = [8 * 128, 128]
+    a.lam = -1.0
+    assert lib.blasst_attn_decode(ctypes.byref(a), None, 0, None) == F.BLASST_ERR_INVALID_ARG
+    a.lam = 0.01
+    a.num_splits = 3
+    assert lib.blasst_attn_decode(ctypes.byref(a), None, 0, None) == F.BLASST_ERR_WORKSPACE
+    a.num_splits = -1
+    assert lib.blasst_attn_decode(ctypes.byref(a), None, 0, None) == F.BLASST_ERR_INVALID_ARG
+    a.num_splits = 1
+    a.heads_kv = 3
+    assert lib.blasst_attn_decode(ctypes.byref(a), None, 0, None) == F.BLASST_ERR_INVALID_ARG

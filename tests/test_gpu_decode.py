@@ -1,0 +1,130 @@
+"""GPU parity of blasst_attn_decode (GQA / MQA / MLA-shaped) against the fp64 oracle."""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import flashattention_softmax_threshold_amd as F
+from flashattention_softmax_threshold_amd.inputs import decode_inputs
+
+from parity import (assert_lse_close, assert_outputs_close, compare_tile_status, need_gpu,
+                    oracle_scale)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_gpu(q, k, v, kv_len, *, lam, num_splits=0, block_r=0):
+    B, Hq, Dqk = q.shape
+    br, bc, S = F.blasst_decode_plan(q, k, v, block_r=block_r, num_splits=num_splits)
+    Hkv = k.shape[2]
+    n_rb = -(-(Hq // Hkv) // br)
+    nt = -(-k.shape[1] // bc)
+    ts = torch.full((B, Hkv, n_rb, max(nt, 1)), 255, dtype=torch.uint8, device=q.device)
+    tm = torch.zeros((B, Hkv, n_rb, max(nt, 1)), dtype=torch.float32, device=q.device)
+    lse = torch.zeros((B, Hq), dtype=torch.float32, device=q.device)
+    cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
+    o = F.blasst_attn_decode(q, k, v, kv_len=kv_len, lam=lam, lse=lse, counters=cnt,
+                             tile_status=ts, tile_margin=tm, block_r=block_r,
+                             num_splits=num_splits)
+    torch.cuda.synchronize()
+    return dict(o=o, lse=lse, status=ts.cpu().numpy(), margin=tm.cpu().numpy(),
+                counters=cnt.cpu().tolist(), br=br, bc=bc, splits=S)
+
+
+def _check(res, ref, q, lam, what, kv_len):
+    o_gpu = res["o"].float().cpu().numpy().astype(np.float64)
+    lse_gpu = res["lse"].cpu().numpy().astype(np.float64)
+    G = q.shape[1] // res["status"].shape[1]
+    br = res["br"]
+    og, orf, lg, lr = [], [], [], []
+    band_mism = 0
+    for (b, g, rb), u in ref.units.items():
+        h0 = g * G + rb * br
+        rows = u.o.shape[0]
+        og.append(o_gpu[b, h0:h0 + rows])
+        orf.append(u.o)
+        lg.append(lse_gpu[b, h0:h0 + rows])
+        lr.append(u.lse)
+        nt = len(u.tile_status)
+        st = res["status"][b, g, rb]
+        m, _ = compare_tile_status(st[:nt], u.tile_status, u.tile_margin, lam,
+                                   f"{what} unit {(b, g, rb)}")
+        band_mism += m
+        assert np.all(st[nt:] == 2), f"{what}: tiles past kv_len must be 'not visited'"
+    assert_outputs_close(np.concatenate(og), np.concatenate(orf), q.dtype, what)
+    assert_lse_close(np.concatenate(lg), np.concatenate(lr), q.dtype, what)
+    return band_mism
+
+
+def _case(B, Hq, Hkv, L, D, kv_len, lams, splits, beta, share, seed, block_r=0, Dv=None,
+          cluster_len=100):
+    need_gpu()
+    Dv = D if Dv is None else Dv
+    mla = Dv != D
+    q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=Hkv, L=L, d_qk=D, d_v=Dv, cluster_len=cluster_len,
+                                 dtype=torch.bfloat16, seed=seed, beta=beta, share=share,
+                                 v_aliases_k=mla, kv_len=kv_len)
+    # Head-major cache storage on the device, as the generator lays it out.
+    kd = k.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    if mla:
+        vd = kd[..., :Dv]
+    else:
+        vd = v.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    qd, kvd = q.cuda(), kvl.cuda()
+    skipped = 0
+    for S in splits:
+        for lam in lams:
+            what = f"decode B{B} H{Hq}/{Hkv} L{L} d{D}/{Dv} S={S} beta={beta} lam={lam}"
+            print(what, flush=True)
+            res = _run_gpu(qd, kd, vd, kvd, lam=lam, num_splits=S, block_r=block_r)
+            ref = oracle.decode(q, k, v, kv_len=kvl, block_r=res["br"], block_c=res["bc"],
+                                num_splits=res["splits"], scale=oracle_scale(D), lam=lam,
+                                threads=8)
+            band_mism = _check(res, ref, q, lam, what, kvl)
+            assert res["counters"][0] == ref.visited
+            assert abs(res["counters"][1] - ref.skipped) <= band_mism
+            skipped += ref.skipped
+    return skipped
+
+
+def test_gqa_small_lengths_and_splits():
+    L = 1000
+    kv_len = [1000, 1, 577]
+    lams = [0.0, 16 / L, 64 / L, 1.0]
+    _case(3, 8, 2, L, 128, kv_len, lams[:2], (1, 3), 1.0, False, seed=21)
+    assert _case(3, 8, 2, L, 128, kv_len, lams, (1, 3, 7), 16.0, False, seed=22) > 0
+
+
+def test_gqa_empty_sequence_d64_and_odd_group():
+    # kv_len 0 gives o = 0, lse = -inf; head dim 64; 3 query heads per KV head (padded rows).
+    _case(2, 6, 2, 300, 64, [0, 300], [0.0, 0.05], (1, 2), 8.0, True, seed=23)
+    assert _case(2, 6, 2, 300, 128, [129, 300], [0.0, 0.2], (1,), 8.0, True, seed=24) > 0
+
+
+def test_mqa_two_row_blocks():
+    assert _case(2, 32, 1, 700, 128, None, [0.0, 0.02], (1, 2), 16.0, True, seed=25) > 0
+
+
+def test_gqa_decode_full_size_sampled():
+    """GQA decode at full size: 64 sequences x 32/8 heads, KV length 32768, d 128."""
+    need_gpu()
+    B, Hq, Hkv, L = 64, 32, 8, 32768
+    q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=Hkv, L=L, d_qk=128, d_v=128, cluster_len=512,
+                                 dtype=torch.bfloat16, device="cuda", seed=3000, beta=16.0)
+    rng = random.Random(3)
+    units = [(0, 0, 0), (63, 7, 0)] + [(rng.randrange(B), rng.randrange(Hkv), 0) for _ in range(6)]
+    for a in (4, 16, 64):
+        lam = a / L
+        what = f"C3 lam={a}/L"
+        print(what, flush=True)
+        res = _run_gpu(q, k, v, kvl, lam=lam)
+        ref = oracle.decode(q, k, v, kv_len=kvl, block_r=res["br"], block_c=res["bc"],
+                            num_splits=res["splits"], scale=oracle_scale(128), lam=lam,
+                            units=units, threads=16)
+        _check(res, ref, q, lam, what, kvl)
+        st = res["status"]
+        assert res["counters"][0] == int((st != 2).sum())
+        assert res["counters"][1] == int((st == 1).sum())
+        assert ref.skipped > 0

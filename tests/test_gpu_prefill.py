@@ -1,0 +1,151 @@
+"""GPU parity of blasst_attn_prefill against the fp64 oracle, element by element."""
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import flashattention_softmax_threshold_amd as F
+from flashattention_softmax_threshold_amd.inputs import prefill_inputs
+
+from parity import (assert_lse_close, assert_outputs_close, compare_tile_status, need_gpu,
+                    oracle_scale)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_gpu(q, k, v, *, causal, lam, block_r=0):
+    B, Lq, Hq, D = q.shape
+    br, bc = F.blasst_prefill_tiles(q, k, block_r=block_r)
+    nqb, nkt = -(-Lq // br), -(-k.shape[1] // bc)
+    ts = torch.full((B, Hq, nqb, nkt), 255, dtype=torch.uint8, device=q.device)
+    tm = torch.zeros((B, Hq, nqb, nkt), dtype=torch.float32, device=q.device)
+    lse = torch.zeros((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
+    o = F.blasst_attn_prefill(q, k, v, causal=causal, lam=lam, lse=lse, counters=cnt,
+                              tile_status=ts, tile_margin=tm, block_r=block_r)
+    torch.cuda.synchronize()
+    return dict(o=o, lse=lse, status=ts.cpu().numpy(), margin=tm.cpu().numpy(),
+                counters=cnt.cpu().tolist(), br=br, bc=bc)
+
+
+def _check_units(res, ref, q, lam, what, units=None):
+    """Compare the oracle's units with the GPU outputs of the same units."""
+    o_gpu = res["o"].float().cpu().numpy().astype(np.float64)
+    lse_gpu = res["lse"].cpu().numpy().astype(np.float64)
+    br = res["br"]
+    og, orf, lg, lr = [], [], [], []
+    band_mism = band = 0
+    for (b, h, qb), u in ref.units.items():
+        r0 = qb * br
+        rows = u.o.shape[0]
+        og.append(o_gpu[b, r0:r0 + rows, h])
+        orf.append(u.o)
+        lg.append(lse_gpu[b, h, r0:r0 + rows])
+        lr.append(u.lse)
+        nt = len(u.tile_status)
+        m, n = compare_tile_status(res["status"][b, h, qb, :nt], u.tile_status,
+                                   u.tile_margin, lam, f"{what} unit {(b, h, qb)}")
+        band_mism += m
+        band += n
+    o_g, o_r = np.concatenate(og), np.concatenate(orf)
+    err = assert_outputs_close(o_g, o_r, q.dtype, what)
+    assert_lse_close(np.concatenate(lg), np.concatenate(lr), q.dtype, what)
+    return err, band_mism, band
+
+
+def _case(B, L, Hq, Hkv, D, dtype, causal, block_r, beta, lams, seed, cluster_len=64, sinks=0):
+    need_gpu()
+    q, k, v = prefill_inputs(B=B, L=L, Hq=Hq, Hkv=Hkv, d=D, cluster_len=cluster_len, dtype=dtype,
+                             seed=seed, beta=beta, sinks=sinks)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    skipped_any = False
+    for lam in lams:
+        what = f"prefill B{B} L{L} H{Hq}/{Hkv} d{D} {dtype} causal={causal} br={block_r} beta={beta} lam={lam}"
+        print(what, flush=True)
+        res = _run_gpu(qd, kd, vd, causal=causal, lam=lam, block_r=block_r)
+        ref = oracle.prefill(q, k, v, causal=causal, block_r=res["br"], block_c=res["bc"],
+                             scale=oracle_scale(D), lam=lam, threads=8)
+        _, band_mism, _ = _check_units(res, ref, q, lam, what)
+        # Counters: the oracle's totals, up to decisions inside the margin band.
+        assert res["counters"][0] == ref.visited
+        assert abs(res["counters"][1] - ref.skipped) <= band_mism
+        skipped_any |= ref.skipped > 0
+    return skipped_any
+
+
+def test_tiny_fp32_mha_all_lambdas():
+    """The tiny fp32 workload: B1 H2 L512 d64, tile 64x64, lambda in {0, 1e-3, 1e-2, 1e-1}."""
+    lams = [0.0, 1e-3, 1e-2, 1e-1]
+    _case(1, 512, 2, 2, 64, torch.float32, False, 64, 1.0, lams, seed=1000)
+    assert _case(1, 512, 2, 2, 64, torch.float32, False, 64, 8.0, lams, seed=1001)
+
+
+@pytest.mark.parametrize("block_r", [128, 64, 32])
+def test_bf16_causal_gqa_ragged(block_r):
+    L = 700
+    lams = [0.0, 4 / L, 64 / L, 1.0, 5.0]
+    _case(2, L, 8, 2, 128, torch.bfloat16, True, block_r, 1.0, lams[:2], seed=7, sinks=16)
+    assert _case(2, L, 8, 2, 128, torch.bfloat16, True, block_r, 32.0, lams, seed=8,
+                 cluster_len=128, sinks=16)
+
+
+def test_bf16_noncausal_d64_and_fp32_causal_d128():
+    assert _case(1, 333, 4, 4, 64, torch.bfloat16, False, 128, 16.0, [0.0, 0.01, 0.3], seed=9)
+    assert _case(1, 200, 2, 1, 128, torch.float32, True, 64, 16.0, [0.0, 0.05], seed=10)
+
+
+def test_edge_lengths():
+    # A single key, fewer rows than a block, lengths one past a tile.
+    _case(1, 1, 2, 1, 128, torch.bfloat16, False, 128, 8.0, [0.0, 0.5], seed=11)
+    _case(3, 65, 2, 2, 64, torch.bfloat16, True, 64, 8.0, [0.0, 0.5], seed=12)
+    _case(1, 129, 4, 2, 128, torch.float32, False, 32, 8.0, [0.0, 1.0], seed=13)
+
+
+def _sampled_full_size(q, k, v, causal, lam, units, what):
+    res = _run_gpu(q, k, v, causal=causal, lam=lam)
+    ref = oracle.prefill(q, k, v, causal=causal, block_r=res["br"], block_c=res["bc"],
+                         scale=oracle_scale(q.shape[3]), lam=lam, units=units, threads=16)
+    err, band_mism, band = _check_units(res, ref, q, lam, what)
+    # Whole-call counters agree with the whole-call tile map the kernel wrote.
+    st = res["status"]
+    assert res["counters"][0] == int((st != 2).sum())
+    assert res["counters"][1] == int((st == 1).sum())
+    return res, ref
+
+
+@pytest.mark.parametrize("beta", [1.0, 32.0])
+def test_causal_gqa_8k_full_size_sampled(beta):
+    """Causal GQA prefill at full size (B1, 32/8 heads, L 8192, d 128, tile 128x64)."""
+    need_gpu()
+    L = 8192
+    q, k, v = prefill_inputs(B=1, L=L, Hq=32, Hkv=8, d=128, cluster_len=256,
+                             dtype=torch.bfloat16, device="cuda", seed=2000, beta=beta, sinks=64)
+    rng = random.Random(5)
+    units = [(0, 0, 0), (0, 31, 63), (0, 5, 63)] + [(0, rng.randrange(32), rng.randrange(64))
+                                                    for _ in range(9)]
+    for a in (4, 16, 64):
+        what = f"C2 beta={beta} lam={a}/L"
+        print(what, flush=True)
+        res, ref = _sampled_full_size(q, k, v, True, a / L, units, what)
+        if beta > 1:
+            assert ref.skipped > 0
+
+
+@pytest.mark.parametrize("beta", [1.0, 4.0])
+def test_video_dit_full_size_sampled(beta):
+    """Video-DiT self-attention at full size (40 heads, L 75600 = 21 frames x 3600, d 128)."""
+    need_gpu()
+    L = 75600
+    q, k, v = prefill_inputs(B=1, L=L, Hq=40, Hkv=40, d=128, cluster_len=60,
+                             dtype=torch.bfloat16, device="cuda", seed=4000, beta=beta,
+                             frame_len=3600, patch_len=60)
+    a, b = 2822.6209952221557, 4.388250623520793
+    units = [(0, 0, 0), (0, 39, 590), (0, 17, 300), (0, 3, 77)]
+    for s in (0.5, 0.7):
+        lam = F.blasst_resolve_lambda(F.BLASST_TARGET_SPARSITY, L, target_sparsity=s, a=a, b=b)
+        what = f"C4 beta={beta} s={s} lam={lam:.4f}"
+        print(what, flush=True)
+        _sampled_full_size(q, k, v, False, lam, units, what)
