@@ -59,6 +59,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float sP[4][64][RB];
   __shared__ __attribute__((aligned(16))) float sO[4][RB][D];
   __shared__ float sL[4][16];
+  __shared__ float sM[16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mt2 = (n < nrows) ? mt * p.scale_log2 : -INFINITY;
+    const float mt2 = (n < nrows) ? __fmul_rn(mt, p.scale_log2) : -INFINITY;
     if (lane < 16) sT[r & 1][wv][lane] = mt2;
     __syncthreads();
 
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
     for (int w = 0; w < 4; ++w) {
       const float tm = sT[r & 1][w][n];
       const float m2 = fmaxf(mp, tm);
-      const float dl = tm - m2;
+      const float dl = (tm >= mp) ? 0.f : __fsub_rn(tm, mp);  // exactly 0 for a new row maximum
       const bool valid = (n < nrows) && tm > -INFINITY;
       keep_w[w] = __ballot(valid && !(dl < p.tau_log2)) != 0ull;
       if (w == wv) dmy = valid ? dl : -INFINITY;
@@ -184,12 +185,15 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
       }
     }
     const float M_use = (M == -INFINITY) ? 0.f : M;
-    const float alpha = exp2_fast(m_run - M_use);
+    const float alpha = exp2_fast(m_run - M_use);  // for this lane's row n
     l_part *= alpha;
+    // O is held column-wise (every lane has all rows): row rr's factor comes from lane rr.
 #pragma unroll
-    for (int rr = 0; rr < RB; ++rr)
+    for (int rr = 0; rr < RB; ++rr) {
+      const float a_r = __shfl(alpha, rr);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[rr][e] *= alpha;
+      for (int e = 0; e < 8; ++e) o[rr][e] *= a_r;
+    }
 
     if (my_keep) {
       float ps = 0.f;
@@ -263,6 +267,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
   lrow += __shfl_xor(lrow, 16);
   lrow += __shfl_xor(lrow, 32);
   if (lane < 16) sL[wv][lane] = lrow;
+  if (wv == 0 && lane < 16) sM[lane] = m_run;  // every wave holds the same running maxima
   __syncthreads();
 
   for (int idx = tid; idx < nrows * D; idx += 256) {
@@ -270,15 +275,16 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
     const float L = sL[0][rr] + sL[1][rr] + sL[2][rr] + sL[3][rr];
     const float acc = sO[0][rr][d] + sO[1][rr][d] + sO[2][rr][d] + sO[3][rr][d];
     const float val = L > 0.f ? acc / L : 0.f;
+    const float m_row = sM[rr];
     const int h = h0 + rr;
     if (p.num_splits == 1) {
       ((__bf16 *)p.o)[b * p.o_sb + (int64_t)h * p.o_sh + d] = (__bf16)val;
       if (d == 0 && p.lse)
-        p.lse[(int64_t)b * p.Hq + h] = L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY;
+        p.lse[(int64_t)b * p.Hq + h] = L > 0.f ? (m_row + __log2f(L)) * kLn2 : -INFINITY;
     } else {
       const int64_t row = ((int64_t)b * p.Hq + h) * p.num_splits + split;
       p.o_part[row * D + d] = val;
-      if (d == 0) p.lse_part[row] = L > 0.f ? m_run + __log2f(L) : -INFINITY;
+      if (d == 0) p.lse_part[row] = L > 0.f ? m_row + __log2f(L) : -INFINITY;
     }
   }
   if (lane == 0 && p.counters && visited) {

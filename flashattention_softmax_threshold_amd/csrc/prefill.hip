@@ -248,9 +248,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mt2 = mt * p.scale_log2;
+    // The row's margin tile_max - running_max (<= 0). mt2 is rounded on its own (no fused
+    // multiply-add with the subtraction), and a tile holding a new row maximum gets exactly 0:
+    // otherwise a contracted product could leave the new maximum a hair below 0, the row would
+    // vote "skip" at lambda = 1, and the skipped tile would hold a running maximum it never set.
+    const float mt2 = __fmul_rn(mt, p.scale_log2);
     const float m_new = fmaxf(m_run, mt2);
-    const float delta = mt2 - m_new;  // <= 0; the tile's margin for this row
+    const float delta = (mt2 >= m_run) ? 0.f : __fsub_rn(mt2, m_run);
     const bool has_key = mt2 > -INFINITY;
     const bool keep_row = row_ok && has_key && !(delta < p.tau_log2);
     const unsigned long long ballot = __ballot(keep_row);

@@ -64,6 +64,7 @@ class _Unit(ctypes.Structure):
         ("tile_status", ctypes.c_void_p),
         ("tile_margin", ctypes.c_void_p),
         ("max_tiles", ctypes.c_int),
+        ("forced", ctypes.c_void_p),
         ("visited", ctypes.c_longlong),
         ("skipped", ctypes.c_longlong),
         ("status", ctypes.c_int),
@@ -83,7 +84,7 @@ def _load():
             lib.oracle_dense_rows.argtypes = [I, I, I, I, P, P, P, P, D, P, P]
             lib.oracle_dense_rows.restype = I
             lib.oracle_blasst_rows.argtypes = [I, I, I, P, P, P, P, I, I, I, D, D, P, P, P, P,
-                                               P, P, P, P, I]
+                                               P, P, P, P, I, P]
             lib.oracle_blasst_rows.restype = I
             lib.oracle_combine.argtypes = [I, I, I, P, P, P, P]
             lib.oracle_combine.restype = I
@@ -138,11 +139,12 @@ def dense_rows(q, k, v, row_keys, scale: float):
 
 
 def blasst_rows(q, k, v, row_keys, k_begin: int, k_end: int, block_c: int, scale: float,
-                lam: float):
+                lam: float, forced=None):
     """Tiled BLASST loop of one row block over keys [k_begin, k_end) (see blasst_oracle.c).
 
     Returns a dict with o, lse, m (final running max), l (final running sum), visited, skipped,
-    tile_status and tile_margin (one entry per tile of the range).
+    tile_status and tile_margin (one entry per tile of the range). ``forced``: optional per-tile
+    decisions (TILE_SKIPPED = skip) imposed instead of the test.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     rk = np.ascontiguousarray(np.asarray(row_keys, dtype=np.int32))
@@ -157,10 +159,16 @@ def blasst_rows(q, k, v, row_keys, k_begin: int, k_end: int, block_c: int, scale
     tm = np.zeros(max(n_tiles, 1))
     vis = ctypes.c_longlong(0)
     sk = ctypes.c_longlong(0)
+    fz = None
+    if forced is not None:
+        fz = np.ascontiguousarray(np.asarray(forced, dtype=np.uint8)[:n_tiles])
+        if fz.shape[0] < n_tiles:
+            raise ValueError("forced decisions must cover every tile of the range")
     rc = _load().oracle_blasst_rows(R, dqk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(rk), int(k_begin),
                                     int(k_end), int(block_c), float(scale), float(lam), _ptr(o),
                                     _ptr(lse), _ptr(m), _ptr(l), ctypes.byref(vis),
-                                    ctypes.byref(sk), _ptr(ts), _ptr(tm), n_tiles)
+                                    ctypes.byref(sk), _ptr(ts), _ptr(tm), n_tiles,
+                                    _ptr(fz) if fz is not None else None)
     _check(rc, "oracle_blasst_rows")
     return dict(o=o, lse=lse, m=m, l=l, visited=vis.value, skipped=sk.value,
                 tile_status=ts[:n_tiles].copy(), tile_margin=tm[:n_tiles].copy())
@@ -214,28 +222,34 @@ class _Batch:
         self.entries = []  # (key, split index, arrays)
         self.bytes = 0
 
-    def add(self, key, split, q, k, v, row_keys, k_begin, k_end):
+    def add(self, key, split, q, k, v, row_keys, k_begin, k_end, forced=None):
         R = q.shape[0]
         n_tiles = max(0, -(-(k_end - k_begin) // self.block_c))
+        if forced is not None:
+            forced = np.ascontiguousarray(np.asarray(forced, dtype=np.uint8)[:n_tiles])
+            if forced.shape[0] < n_tiles:
+                raise ValueError("forced decisions must cover every tile of the range")
         o = np.zeros((R, self.d_v))
         lse = np.zeros(R)
         ts = np.zeros(max(n_tiles, 1), dtype=np.uint8)
         tm = np.zeros(max(n_tiles, 1))
         rk = np.ascontiguousarray(np.asarray(row_keys, dtype=np.int32))
-        self.keep.append((q, k, v, rk))
-        self.entries.append((key, split, R, q, k, v, rk, k_begin, k_end, o, lse, ts, tm, n_tiles))
+        self.keep.append((q, k, v, rk, forced))
+        self.entries.append((key, split, R, q, k, v, rk, k_begin, k_end, o, lse, ts, tm, n_tiles,
+                             forced))
 
     def run(self, sink):
         if not self.entries:
             return
         units = (_Unit * len(self.entries))()
         for i, e in enumerate(self.entries):
-            key, split, R, q, k, v, rk, kb, ke, o, lse, ts, tm, nt = e
+            key, split, R, q, k, v, rk, kb, ke, o, lse, ts, tm, nt, fz = e
             u = units[i]
             u.n_rows, u.q, u.k, u.v, u.row_keys = R, q.ctypes.data, k.ctypes.data, v.ctypes.data, rk.ctypes.data
             u.k_begin, u.k_end = kb, ke
             u.o, u.lse = o.ctypes.data, lse.ctypes.data
             u.tile_status, u.tile_margin, u.max_tiles = ts.ctypes.data, tm.ctypes.data, nt
+            u.forced = fz.ctypes.data if fz is not None else None
         lib = _load()
         if self.dense:
             rc = lib.oracle_dense_batch(len(self.entries), ctypes.cast(units, ctypes.c_void_p),
@@ -246,7 +260,7 @@ class _Batch:
                                          float(self.lam), int(self.threads))
         _check(rc, "oracle batch")
         for i, e in enumerate(self.entries):
-            key, split, R, q, k, v, rk, kb, ke, o, lse, ts, tm, nt = e
+            key, split, R, q, k, v, rk, kb, ke, o, lse, ts, tm, nt, _ = e
             sink(key, split, UnitResult(o, lse, units[i].visited, units[i].skipped,
                                         ts[:nt].copy(), tm[:nt].copy()))
         self.keep.clear()
@@ -258,12 +272,13 @@ def _as_shape(x):
 
 
 def prefill(q, k, v, *, causal: bool, block_r: int, block_c: int, scale: float, lam: float,
-            units=None, threads: int = 0, dense: bool = False,
+            units=None, threads: int = 0, dense: bool = False, forced=None,
             budget_bytes: int = 1 << 30) -> CallResult:
     """Oracle of a prefill call. q: [B, Lq, Hq, d_qk], k: [B, Lkv, Hkv, d_qk], v: [B, Lkv, Hkv, d_v].
 
     units: iterable of (b, h, qb) or None for every unit. dense=True evaluates the dense
-    definition instead of the tiled loop (tile fields are then empty).
+    definition instead of the tiled loop (tile fields are then empty). forced: optional dict
+    unit -> per-tile decisions imposed instead of the test (see blasst_rows).
     """
     B, Lq, Hq, dqk = _as_shape(q)
     _, Lkv, Hkv, _ = _as_shape(k)
@@ -300,7 +315,8 @@ def prefill(q, k, v, *, causal: bool, block_r: int, block_c: int, scale: float, 
             row_keys = [min(p + 1, Lkv) for p in range(r0, r1)]
         else:
             row_keys = [Lkv] * (r1 - r0)
-        batch.add((b, h, qb), 0, qf, kf, vf, row_keys, 0, Lkv)
+        batch.add((b, h, qb), 0, qf, kf, vf, row_keys, 0, Lkv,
+                  forced.get((b, h, qb)) if forced else None)
     batch.run(sink)
     return result
 
@@ -319,12 +335,14 @@ def split_ranges(kv_len: int, max_kv_len: int, block_c: int, num_splits: int):
 
 def decode(q, k, v, *, kv_len=None, block_r: int, block_c: int, num_splits: int = 1,
            scale: float, lam: float, units=None, threads: int = 0, dense: bool = False,
-           budget_bytes: int = 1 << 30) -> CallResult:
+           forced=None, budget_bytes: int = 1 << 30) -> CallResult:
     """Oracle of a decode call (one query token per sequence).
 
     q: [B, Hq, d_qk], k: [B, L, Hkv, d_qk], v: [B, L, Hkv, d_v]; kv_len: per-sequence lengths
     (None = all L). units: iterable of (b, g, rb) or None for all. Each unit's splits are merged
-    by log-sum-exp; visited/skipped and tile arrays cover all of its splits.
+    by log-sum-exp; visited/skipped and tile arrays cover all of its splits. forced: optional
+    dict unit -> decisions for the unit's tiles 0, 1, ... (absolute tile index), imposed instead
+    of the test.
     """
     B, Hq, dqk = _as_shape(q)
     _, L, Hkv, _ = _as_shape(k)
@@ -361,8 +379,10 @@ def decode(q, k, v, *, kv_len=None, block_r: int, block_c: int, num_splits: int 
         qf = _f64(q[b, h0:h1, :])
         ranges = [(0, kv_len[b])] if (dense or num_splits == 1) else \
             split_ranges(kv_len[b], max_len, block_c, num_splits)
+        fu = forced.get((b, g, rb)) if forced else None
         for s, (a, e) in enumerate(ranges):
-            batch.add((b, g, rb), s, qf, kf, vf, [kv_len[b]] * (h1 - h0), a, e)
+            fs = None if fu is None else np.asarray(fu)[a // block_c:]
+            batch.add((b, g, rb), s, qf, kf, vf, [kv_len[b]] * (h1 - h0), a, e, fs)
     batch.run(sink)
 
     result = CallResult()

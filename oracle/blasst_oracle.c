@@ -118,12 +118,20 @@ int oracle_dense_rows(int n_rows, int n_keys, int d_qk, int d_v, const double *q
  * Outputs: o (n_rows x d_v), lse, row_max, row_sum (the final m and l); visited and skipped
  * tile counts (added to *visited / *skipped); per tile, if the arrays are non-NULL and the tile
  * index is below max_tiles: tile_status (kept / skipped / not visited) and tile_margin.
+ *
+ * forced (may be NULL, else max_tiles entries): take each visited tile's decision from
+ * forced[tile] (ORACLE_TILE_SKIPPED = skip, anything else = keep) instead of the test. The rest of
+ * the pass is unchanged, so this evaluates the method for a given set of decisions; it exists to
+ * check a kernel's output when a tile's margin lies so close to ln(lambda) that float rounding
+ * decided it the other way. A forced skip may drop a tile holding a new row maximum; the running
+ * max then stays where it was, as in the kernel.
  */
 int oracle_blasst_rows(int n_rows, int d_qk, int d_v, const double *q, const double *k,
                        const double *v, const int *row_keys, int k_begin, int k_end,
                        int block_c, double scale, double lambda, double *o, double *lse,
                        double *row_max, double *row_sum, long long *visited, long long *skipped,
-                       unsigned char *tile_status, double *tile_margin, int max_tiles) {
+                       unsigned char *tile_status, double *tile_margin, int max_tiles,
+                       const unsigned char *forced) {
   if (n_rows < 0 || d_qk <= 0 || d_v <= 0 || block_c <= 0 || k_begin < 0 || k_end < k_begin)
     return ORACLE_BAD_ARG;
   if (!(lambda >= 0.0) || isinf(lambda)) return ORACLE_BAD_ARG; /* NaN, negative or infinite */
@@ -187,12 +195,15 @@ int oracle_blasst_rows(int n_rows, int d_qk, int d_v, const double *q, const dou
 
     /* The skip test: every row's margin below ln(lambda) (rows without a key vote skip).
        margin is the largest row margin, so "all rows below tau" is "margin < tau". */
-    if (margin < tau) {
+    int skip = margin < tau;
+    if (forced && tile < max_tiles) skip = forced[tile] == ORACLE_TILE_SKIPPED;
+    if (skip) {
       *skipped += 1;
       if (tile_status && tile < max_tiles) tile_status[tile] = ORACLE_TILE_SKIPPED;
       /* With lambda <= 1 a skipped tile cannot hold a new row maximum. */
-      for (int r = 0; r < n_rows; ++r)
-        if (mt[r] > m[r]) status = ORACLE_SKIP_RAISED_MAX;
+      if (!forced)
+        for (int r = 0; r < n_rows; ++r)
+          if (mt[r] > m[r]) status = ORACLE_SKIP_RAISED_MAX;
       continue;
     }
     if (tile_status && tile < max_tiles) tile_status[tile] = ORACLE_TILE_KEPT;
@@ -284,6 +295,7 @@ typedef struct {
   unsigned char *tile_status; /* may be NULL */
   double *tile_margin;        /* may be NULL */
   int max_tiles;
+  const unsigned char *forced; /* may be NULL: decisions to impose (see oracle_blasst_rows) */
   long long visited, skipped; /* outputs */
   int status;                 /* output */
 } oracle_unit;
@@ -305,7 +317,8 @@ int oracle_blasst_batch(int n_units, oracle_unit *units, int d_qk, int d_v, int 
     un->status = oracle_blasst_rows(un->n_rows, d_qk, d_v, un->q, un->k, un->v, un->row_keys,
                                     un->k_begin, un->k_end, block_c, scale, lambda, un->o,
                                     un->lse, NULL, NULL, &un->visited, &un->skipped,
-                                    un->tile_status, un->tile_margin, un->max_tiles);
+                                    un->tile_status, un->tile_margin, un->max_tiles,
+                                    un->forced);
   }
   for (int u = 0; u < n_units; ++u)
     if (units[u].status != ORACLE_OK) worst = units[u].status;

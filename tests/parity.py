@@ -3,8 +3,9 @@
 Bar (bf16 inputs, fp32 accumulation): max|dO| <= 1e-2 * max|O| and mean|dO| <= 1e-3 over the
 compared outputs; LSE within 1e-2 (natural log). fp32 inputs: max|dO| <= 1e-4 * max|O|,
 mean|dO| <= 1e-5, LSE within 1e-4. Skip decisions must agree exactly on every tile whose oracle
-margin lies at least 1e-3 away from ln(lambda); inside that band float rounding may flip the
-decision, and such tiles are counted, not failed.
+margin lies outside a band around ln(lambda); inside the band float rounding may flip the
+decision, and such tiles are counted, not failed (their units are then compared against the
+oracle evaluated with the kernel's decisions).
 """
 from __future__ import annotations
 
@@ -51,13 +52,13 @@ def assert_lse_close(lse_gpu: np.ndarray, lse_ref: np.ndarray, dtype, what: str)
 
 
 def compare_tile_status(st_gpu: np.ndarray, st_ref: np.ndarray, margin_ref: np.ndarray,
-                        lam: float, what: str):
+                        lam: float, what: str, band_width: float = MARGIN_BAND):
     """Exact agreement outside the margin band; returns (#mismatches inside the band, #band)."""
     st_gpu = np.asarray(st_gpu).ravel()
     st_ref = np.asarray(st_ref).ravel()
     margin_ref = np.asarray(margin_ref).ravel()
     t = tau(lam)
-    band = np.isfinite(margin_ref) & (np.abs(margin_ref - t) < MARGIN_BAND) if math.isfinite(t) \
+    band = np.isfinite(margin_ref) & (np.abs(margin_ref - t) < band_width) if math.isfinite(t) \
         else np.zeros_like(st_ref, dtype=bool)
     mism = st_gpu != st_ref
     bad = mism & ~band

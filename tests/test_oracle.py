@@ -351,3 +351,25 @@ def test_decode_units_and_splits_follow_closed_form():
             o_ref = (w[:, :, None] * np.array(os_)).sum(0) / w.sum(0)[:, None]
             np.testing.assert_allclose(u.o, o_ref, rtol=1e-10, atol=1e-11)
     assert any_skip > 0
+
+
+def test_forced_decisions_mode():
+    """Imposing decisions: the test's own decisions change nothing; 'keep all' is the dense
+    result; any other set gives the softmax over exactly the kept tiles."""
+    rng = np.random.default_rng(44)
+    q, k, v = _clustered_rows(rng, 5, 300, 16, 4, beta=8.0)
+    rk = [300] * 5
+    base = oracle.blasst_rows(q, k, v, rk, 0, 300, 32, 0.25, 0.05)
+    same = oracle.blasst_rows(q, k, v, rk, 0, 300, 32, 0.25, 0.05, forced=base["tile_status"])
+    np.testing.assert_array_equal(same["o"], base["o"])
+    keep_all = oracle.blasst_rows(q, k, v, rk, 0, 300, 32, 0.25, 0.05,
+                                  forced=np.zeros(10, dtype=np.uint8))
+    o_ref, _ = _library_attention(q, k, v, rk, 0.25)
+    np.testing.assert_allclose(keep_all["o"], o_ref, rtol=1e-11, atol=1e-12)
+    pattern = np.array([0, 1, 1, 0, 1, 0, 0, 1, 1, 0], dtype=np.uint8)
+    r = oracle.blasst_rows(q, k, v, rk, 0, 300, 32, 0.25, 0.05, forced=pattern)
+    cols = np.repeat(pattern == 0, 32)[:300]
+    s = _masked_scores(q, k, rk, 0.25)
+    o_cf = softmax(np.where(cols[None, :], s, -np.inf), axis=1) @ v
+    np.testing.assert_allclose(r["o"], o_cf, rtol=1e-10, atol=1e-11)
+    assert r["skipped"] == int(pattern.sum())
