@@ -1,0 +1,252 @@
+"""Benchmark of the BLASST skip-softmax attention forward pass on one MI355X.
+
+Headline step: one causal GQA prefill call (batch 1, 32 query / 8 KV heads, L = 8192, head dim
+128, bf16, tile 128 x 64) at lambda = 16 / L on clustered synthetic inputs whose centre gain puts
+the skip fraction in the pages' 50-75 % range. Printed as ONE JSON line:
+
+  value     dense-equivalent TFLOP/s = 4 * Hq * d * L (L + 1) / 2 / (time per call)
+  roofline  the prefill kernel against the bf16 MFMA peak: executed-tile FLOP per call
+            (2 * 128 * 64 * 128 per visited tile for Q K^T, the same per kept tile for P V)
+            / kernel time from HIP events on the launch stream
+  cpu_baseline  the fp64 oracle on a time-bounded random sample of the same call's work units
+            (host cores), in the same unit
+
+Secondary measurements (same line): lambda = 0 on the same kernel and data (speedup), the other
+two thresholds, the literal generator (centre gain 1, nothing skipped), and GQA decode
+(64 x 32/8 heads, KV 32768, d 128) in GB/s against HBM.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import random
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+
+PREFILL = dict(B=1, Hq=32, Hkv=8, L=8192, d=128, cluster_len=256, sinks=64, seed=2000)
+PREFILL_BETA = 32.0   # centre gain giving ~60 % skipped tiles (1.0 = recipe read literally)
+DECODE = dict(B=64, Hq=32, Hkv=8, L=32768, d=128, cluster_len=512, seed=3000)
+DECODE_BETA = 16.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
+    return ap.parse_args()
+
+
+def _time_calls(fn, steps, warmup, stream):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per call
+
+
+def _prefill_counts(F, q, k, v, lam):
+    import torch
+
+    cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
+    F.blasst_attn_prefill(q, k, v, causal=True, lam=lam, counters=cnt)
+    torch.cuda.synchronize()
+    visited, skipped = (int(x) for x in cnt.cpu().tolist())
+    return visited, skipped
+
+
+def _kernel_source_hash(name):
+    path = os.path.join(ROOT, "flashattention_softmax_threshold_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _traffic_from_profile(kernel_file, profile_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != _kernel_source_hash(kernel_file):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _cpu_baseline(q, k, v, lam, br, bc, budget_s=12.0):
+    """The oracle on a random sample of prefill units, until about budget_s seconds passed."""
+    import oracle
+
+    B, L, Hq, d = q.shape
+    n_qb = -(-L // br)
+    units = [(0, h, qb) for h in range(Hq) for qb in range(n_qb)]
+    random.Random(7).shuffle(units)
+    threads = min(16, os.cpu_count() or 1)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    done = []
+    t0 = time.perf_counter()
+    i = 0
+    while i < len(units) and time.perf_counter() - t0 < budget_s:
+        chunk = units[i:i + 64]
+        oracle.prefill(qc, kc, vc, causal=True, block_r=br, block_c=bc, scale=1 / math.sqrt(d),
+                       lam=lam, units=chunk, threads=threads)
+        done += chunk
+        i += 64
+    elapsed = time.perf_counter() - t0
+    # Dense-equivalent FLOP of the sampled units: 4 d per (row, visible key).
+    flops = 0.0
+    for (_, _, qb) in done:
+        r0, r1 = qb * br, min((qb + 1) * br, L)
+        flops += 4.0 * d * sum(r + 1 for r in range(r0, r1))
+    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s (dense-equivalent)", cores=threads,
+                kind="oracle",
+                sample=f"{len(done)} of {len(units)} causal prefill units (random, seed 7), "
+                       f"{elapsed:.1f} s wall, fp64")
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is a design note, not built)"}))
+        sys.exit(2)
+    import torch
+
+    import flashattention_softmax_threshold_amd as F
+    from flashattention_softmax_threshold_amd.inputs import decode_inputs, prefill_inputs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    P = PREFILL
+    L, d, Hq = P["L"], P["d"], P["Hq"]
+    dense_flops = 4.0 * Hq * d * L * (L + 1) / 2
+    q, k, v = prefill_inputs(B=P["B"], L=L, Hq=Hq, Hkv=P["Hkv"], d=d,
+                             cluster_len=P["cluster_len"], dtype=torch.bfloat16, device=dev,
+                             seed=P["seed"], beta=PREFILL_BETA, sinks=P["sinks"])
+    br, bc = F.blasst_prefill_tiles(q, k)
+    tile_flops = 2.0 * br * bc * d
+    o = torch.empty_like(q)
+
+    def prefill_step(lam, qq=q, kk=k, vv=v):
+        return lambda: F.blasst_attn_prefill(qq, kk, vv, causal=True, lam=lam, o=o, stream=stream)
+
+    lam = 16.0 / L
+    ms = _time_calls(prefill_step(lam), args.steps, args.warmup, stream)
+    visited, skipped = _prefill_counts(F, q, k, v, lam)
+    kept = visited - skipped
+    exec_flops = tile_flops * (visited + kept)
+    achieved = exec_flops / (ms * 1e-3) / 1e12
+    traffic = _traffic_from_profile("prefill.hip", "prefill_c2_counters.json")
+    out = {
+        "metric": "attention TFLOP/s (dense-equiv) + % MFMA peak; decode GB/s; skip fraction",
+        "value": dense_flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": f"synthetic clustered (256-token clusters, 64 sink keys, centre gain {PREFILL_BETA})",
+        "config": {"workload": "causal GQA prefill B1 Hq32/Hkv8 L8192 d128 bf16, tile 128x64, "
+                               "lambda=16/L", "batch": 1, "seq_len": L, "heads_q": Hq,
+                   "heads_kv": P["Hkv"], "head_dim": d, "lambda": lam, "tile": [br, bc],
+                   "parallelism": "none (1 GPU)"},
+        "skip_fraction": skipped / visited,
+        "executed_tflops": achieved,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                     "traffic": traffic},
+    }
+
+    if not args.quick:
+        # Same kernel, same data: lambda = 0 and the other thresholds.
+        ms0 = _time_calls(prefill_step(0.0), args.steps, args.warmup, stream)
+        v0, _ = _prefill_counts(F, q, k, v, 0.0)
+        sweep = []
+        for a in (4.0, 16.0, 64.0):
+            la = a / L
+            msa = ms if a == 16.0 else _time_calls(prefill_step(la), args.steps, args.warmup, stream)
+            va, sa = _prefill_counts(F, q, k, v, la)
+            sweep.append({"lambda": f"{int(a)}/L", "ms": msa, "skip_fraction": sa / va,
+                          "speedup_vs_lambda0": ms0 / msa,
+                          "ceiling_2/(2-f)": 2.0 / (2.0 - sa / va),
+                          "executed_tflops": tile_flops * (2 * va - sa) / (msa * 1e-3) / 1e12})
+        out["prefill_lambda0"] = {"ms": ms0, "dense_tflops": dense_flops / (ms0 * 1e-3) / 1e12,
+                                  "executed_tflops": tile_flops * 2 * v0 / (ms0 * 1e-3) / 1e12}
+        out["prefill_sweep"] = sweep
+        # The recipe read literally (centre gain 1): nothing is skipped; overhead of the test.
+        q1, k1, v1 = prefill_inputs(B=P["B"], L=L, Hq=Hq, Hkv=P["Hkv"], d=d,
+                                    cluster_len=P["cluster_len"], dtype=torch.bfloat16,
+                                    device=dev, seed=P["seed"], beta=1.0, sinks=P["sinks"])
+        ms1 = _time_calls(prefill_step(lam, q1, k1, v1), args.steps, args.warmup, stream)
+        ms10 = _time_calls(prefill_step(0.0, q1, k1, v1), args.steps, args.warmup, stream)
+        v1c, s1c = _prefill_counts(F, q1, k1, v1, lam)
+        out["prefill_literal_gain1"] = {"ms": ms1, "ms_lambda0": ms10,
+                                        "skip_fraction": s1c / v1c,
+                                        "speedup_vs_lambda0": ms10 / ms1}
+        del q1, k1, v1
+
+        # GQA decode.
+        D = DECODE
+        qd, kd, vd, kvl = decode_inputs(B=D["B"], Hq=D["Hq"], Hkv=D["Hkv"], L=D["L"], d_qk=D["d"],
+                                        d_v=D["d"], cluster_len=D["cluster_len"],
+                                        dtype=torch.bfloat16, device=dev, seed=D["seed"],
+                                        beta=DECODE_BETA)
+        od = torch.empty((D["B"], D["Hq"], D["d"]), dtype=torch.bfloat16, device=dev)
+        tile_bytes = 64 * D["d"] * 2
+        dec = []
+        msd0 = None
+        for a in (0.0, 4.0, 16.0, 64.0):
+            la = a / D["L"]
+            fn = lambda la=la: F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od,  # noqa: E731
+                                                    stream=stream)
+            msd = _time_calls(fn, args.steps, args.warmup, stream)
+            cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+            F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od, counters=cnt)
+            torch.cuda.synchronize()
+            vis, sk = (int(x) for x in cnt.cpu().tolist())
+            nbytes = tile_bytes * (2 * vis - sk) + qd.numel() * 2 + od.numel() * 2
+            if a == 0.0:
+                msd0 = msd
+            dec.append({"lambda": f"{int(a)}/L", "ms": msd, "skip_fraction": sk / max(vis, 1),
+                        "GB/s": nbytes / (msd * 1e-3) / 1e9,
+                        "hbm_frac": nbytes / (msd * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "speedup_vs_lambda0": msd0 / msd})
+        out["decode_gqa"] = {"workload": "GQA decode B64 Hq32/Hkv8 KV32768 d128 bf16, "
+                                         f"centre gain {DECODE_BETA}", "points": dec}
+        del qd, kd, vd
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(q, k, v, lam, br, bc)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,6 +31,8 @@ struct PrefillParams {
 // dtype: 0 fp32, 1 bf16. Returns hipSuccess or the launch error.
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_dim, int block_r,
                           hipStream_t stream);
+// bf16, B_r = 128: the MFMA kernel with direct-to-LDS tile loads (prefill_mfma.hip).
+hipError_t launch_prefill_mfma(const PrefillParams &p, int head_dim, hipStream_t stream);
 
 struct DecodeParams {
   const void *q, *k, *v;
