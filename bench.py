@@ -48,6 +48,9 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes three times "
+                         "(the reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -135,6 +138,15 @@ def main():
                                    "(multi-GPU sharding is a design note, not built)"}))
         sys.exit(2)
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calibration, "copies": 3}))
+        return
 
     import flashattention_softmax_threshold_amd as F
     from flashattention_softmax_threshold_amd.inputs import decode_inputs, prefill_inputs

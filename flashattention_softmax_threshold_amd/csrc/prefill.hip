@@ -411,7 +411,10 @@ hipError_t launch_d(const PrefillParams &p, int block_r, hipStream_t stream) {
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_dim, int block_r,
                           hipStream_t stream) {
   if (dtype == 1) {
-    if (block_r == 128) return launch_prefill_mfma(p, head_dim, stream);
+    // The MFMA kernel keeps a lane's in-tile byte offset (up to 64 rows of a stride) in 32 bits.
+    const int64_t max_ss = p.k_ss > p.v_ss ? p.k_ss : p.v_ss;
+    if (block_r == 128 && max_ss * 2 * kBlockC + 2 * head_dim < (int64_t(1) << 32))
+      return launch_prefill_mfma(p, head_dim, stream);
     if (head_dim == 64) return launch_d<true, 64>(p, block_r, stream);
     if (head_dim == 128) return launch_d<true, 128>(p, block_r, stream);
   } else {

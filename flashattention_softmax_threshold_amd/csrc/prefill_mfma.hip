@@ -47,6 +47,31 @@ constexpr int kNT = 64 * kNW;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lanes l and l ^ 32 hold the two halves of one query row; v_permlane32_swap exchanges the wave's
+// halves in one VALU op (no LDS round trip).
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max of the 32 scores a lane holds, as a shallow tree.
+__device__ __forceinline__ float max32(const f32x16_t &a, const f32x16_t &b) {
+  float m[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = fmaxf(fmaxf(a[4 * i], a[4 * i + 1]), fmaxf(a[4 * i + 2], a[4 * i + 3]));
+    m[4 + i] = fmaxf(fmaxf(b[4 * i], b[4 * i + 1]), fmaxf(b[4 * i + 2], b[4 * i + 3]));
+  }
+  return fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])),
+               fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
+}
+
 template <int D>
 struct Geo {
   static constexpr int ROW_BYTES = D * 2;                  // one key row of K or V
@@ -65,12 +90,12 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
   using G = Geo<D>;
   constexpr int RB = G::ROW_BYTES, CPR = G::CPR;
   __shared__ __attribute__((aligned(1024))) char smem[2][2][G::TILE_BYTES];  // [stage][K,V]
-  __shared__ int sVote[kNW];
-  __shared__ float sMargin[kNW];
+  __shared__ int sVote[2][kNW];     // per tile parity: the vote of tile j is read one tile later
+  __shared__ float sMargin[2][kNW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar
   const int n = lane & 31;
   const int hh = lane >> 5;
 
@@ -110,23 +135,45 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
   // ---- Tile loads straight into LDS. Wave wv fills rows
   // [wv * LOADS_PER_WAVE * ROWS_PER_LOAD, ...) of each operand; lane L of a load fills row
   // r0 + L / CPR at chunk position L % CPR, fetching logical chunk (L % CPR) ^ swizzle(row).
+  // A lane's byte offset inside a tile is fixed, so it is computed once; per tile only the
+  // scalar base moves (the host guarantees 64 rows of either stride fit in 32 bits).
   const int ld_row_in = lane / CPR;
   const int ld_pc = lane % CPR;
-  auto issue_tile = [&](int j, int st) {
-    const int k0 = j * kBlockC;
+  uint32_t k_off[G::LOADS_PER_WAVE], v_off[G::LOADS_PER_WAVE];
 #pragma unroll
-    for (int t2 = 0; t2 < G::LOADS_PER_WAVE; ++t2) {
-      const int ii = wv * G::LOADS_PER_WAVE + t2;
-      const int r = ii * G::ROWS_PER_LOAD + ld_row_in;
-      const int key = min(k0 + r, p.Lkv - 1);  // rows past the end load a real row; masked later
-      const __bf16 *kp = Kg + (int64_t)key * p.k_ss + 8 * (ld_pc ^ swz_k(r, CPR));
-      const __bf16 *vp = Vg + (int64_t)key * p.v_ss + 8 * (ld_pc ^ swz_v(r, CPR));
-      __builtin_amdgcn_global_load_lds((const void *)kp, (lds_void_t *)(&smem[st][0][ii * 1024]),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)vp, (lds_void_t *)(&smem[st][1][ii * 1024]),
-                                       16, 0, 0);
+  for (int t2 = 0; t2 < G::LOADS_PER_WAVE; ++t2) {
+    const int r = (wv * G::LOADS_PER_WAVE + t2) * G::ROWS_PER_LOAD + ld_row_in;
+    k_off[t2] = (uint32_t)(r * p.k_ss + 8 * (ld_pc ^ swz_k(r, CPR))) * 2u;
+    v_off[t2] = (uint32_t)(r * p.v_ss + 8 * (ld_pc ^ swz_v(r, CPR))) * 2u;
+  }
+  // op 0 = K, 1 = V. Rows past the end of a partial last tile load a real row (masked later).
+  auto issue = [&](int j, int st, int op) {
+    const int k0 = j * kBlockC;
+    const __bf16 *base = op ? Vg : Kg;
+    const int64_t ss = op ? p.v_ss : p.k_ss;
+    if (k0 + kBlockC <= p.Lkv) {
+      const char *tb = (const char *)(base + (int64_t)k0 * ss);
+#pragma unroll
+      for (int t2 = 0; t2 < G::LOADS_PER_WAVE; ++t2) {
+        const int ii = wv * G::LOADS_PER_WAVE + t2;
+        __builtin_amdgcn_global_load_lds((const void *)(tb + (op ? v_off[t2] : k_off[t2])),
+                                         (lds_void_t *)(&smem[st][op][ii * 1024]), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int t2 = 0; t2 < G::LOADS_PER_WAVE; ++t2) {
+        const int ii = wv * G::LOADS_PER_WAVE + t2;
+        const int r = ii * G::ROWS_PER_LOAD + ld_row_in;
+        const int key = min(k0 + r, p.Lkv - 1);
+        const int sw = op ? swz_v(r, CPR) : swz_k(r, CPR);
+        const __bf16 *gp = base + (int64_t)key * ss + 8 * (ld_pc ^ sw);
+        __builtin_amdgcn_global_load_lds((const void *)gp,
+                                         (lds_void_t *)(&smem[st][op][ii * 1024]), 16, 0, 0);
+      }
     }
   };
+  auto issue_k = [&](int j, int st) { issue(j, st, 0); };
+  auto issue_v = [&](int j, int st) { issue(j, st, 1); };
 
   // Per-lane LDS offsets of the MFMA operands.
   // K (A operand of S^T): row 32 kb + n, logical chunk 2 s + hh.
@@ -144,39 +191,50 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
   f32x16_t oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = (f32x16_t)0.f;
-  float m_run = -INFINITY;
-  float l_part = 0.f;
+  float m_run = -INFINITY;  // running row max through the newest scored tile (base-2 units)
+  float m_ref = -INFINITY;  // the max that O and l are currently scaled to
+  float l_part = 0.f;       // this lane's share of the running row sum
   unsigned visited = 0, skipped = 0;
   const int64_t unit_tiles =
       (((int64_t)b * p.Hq + hq) * p.n_qblocks + qb) * (int64_t)p.n_kvtiles;
 
-  issue_tile(0, 0);
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int st = j & 1;
-    const int k0 = j * kBlockC;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile j has landed in LDS
-    __syncthreads();                // ... and every wave's; stage st ^ 1 is free again
-    if (j + 1 < n_tiles) issue_tile(j + 1, st ^ 1);
-
-    // ---- S^T = K Q^T (always: the test needs the scores).
-    f32x16_t sacc[2];
+  // S^T = K Q^T for the tile in K stage st (always computed: the test needs the scores). The K
+  // fragments are read from LDS KPF k-steps ahead of the MFMAs that use them, so LDS latency
+  // hides behind matrix work; the scheduling hints keep that order.
+  auto compute_s = [&](int st, f32x16_t *sacc) {
+    constexpr int NS = D / 16;  // k-steps
+    constexpr int KPF = NS < 2 ? NS : 2;
     sacc[0] = (f32x16_t)0.f;
     sacc[1] = (f32x16_t)0.f;
-    const char *kl = smem[st][0];
+    const char *kl = smem[st][0] + k_rowoff;
+    bf16x8_t fr[NS][2];
+    auto rd = [&](int s) {
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
+      for (int kb = 0; kb < 2; ++kb)
+        fr[s][kb] = *(const bf16x8_t *)(kl + kb * 32 * RB + 16 * ((2 * s + hh) ^ k_swz));
+    };
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t a = *(const bf16x8_t *)(kl + kb * 32 * RB + k_rowoff +
-                                               16 * ((2 * s + hh) ^ k_swz));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-      }
+    for (int s = 0; s < KPF; ++s) rd(s);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + KPF < NS) rd(s + KPF);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s][kb], qf[s], sacc[kb], 0, 0, 0);
     }
+    // Scheduling: KPF steps of reads first, then (2 MFMAs, 2 reads) pairs, then the tail MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KPF, 0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (s + KPF < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
 
-    // ---- Mask: keys past the end, and (causal) keys after the row's position.
-    const bool need_mask = (k0 + kBlockC > p.Lkv) || (p.causal && k0 + kBlockC - 1 > blk_row0);
-    if (need_mask) {
+  // Keys past the end and (causal) keys after the row's position score -inf.
+  auto mask_tile = [&](int j, f32x16_t *sacc) {
+    const int k0 = j * kBlockC;
+    if ((k0 + kBlockC > p.Lkv) || (p.causal && k0 + kBlockC - 1 > blk_row0)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -186,77 +244,137 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
         }
       }
     }
+  };
 
-    // ---- Tile row max, margin, vote. The margin is exactly 0 for a tile holding a new row
-    // maximum (mt2 rounded on its own, no fused multiply-add with the subtraction).
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+  // Tile row max, margin and this wave's vote for tile j (published at the next barrier). The
+  // running max does not depend on any skip decision, so it advances here. The margin is exactly
+  // 0 for a tile holding a new row maximum (mt2 rounded on its own, no fused multiply-add).
+  // Branch-free so it can share a basic block with the previous tile's softmax; every lane
+  // writes the same wave vote. Returns the row's margin (-inf for a row that does not vote).
+  auto vote_tile = [&](int j, const f32x16_t *sacc) {
+    const float mt = max_halves(max32(sacc[0], sacc[1]));
     const float mt2 = __fmul_rn(mt, p.scale_log2);
-    const float m_new = fmaxf(m_run, mt2);
     const float delta = (mt2 >= m_run) ? 0.f : __fsub_rn(mt2, m_run);
+    m_run = fmaxf(m_run, mt2);
     const bool has_key = mt2 > -INFINITY;
     const bool keep_row = row_ok && has_key && !(delta < p.tau_log2);
-    const unsigned long long ballot = __ballot(keep_row);
+    sVote[j & 1][wv] = __ballot(keep_row) != 0ull;
+    return (row_ok && has_key) ? delta : -INFINITY;
+  };
+  // Optional observation: the wave's largest row margin for tile j.
+  auto publish_margin = [&](int j, float dm) {
     if (p.tile_margin) {
-      float dm = (row_ok && has_key) ? delta : -INFINITY;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) dm = fmaxf(dm, __shfl_xor(dm, o));
-      if (lane == 0) sMargin[wv] = dm;
+      sMargin[j & 1][wv] = dm;
     }
-    if (lane == 0) sVote[wv] = ballot != 0ull;
-    __syncthreads();
-    const int keep = sVote[0] | sVote[1] | sVote[2] | sVote[3];
+  };
+
+  auto decision = [&](int j) {
+    const int keep = sVote[j & 1][0] | sVote[j & 1][1] | sVote[j & 1][2] | sVote[j & 1][3];
     if (tid == 0) {
       ++visited;
       skipped += keep ? 0u : 1u;
       if (p.tile_status) p.tile_status[unit_tiles + j] = keep ? 0 : 1;
       if (p.tile_margin) {
-        const float dm = fmaxf(fmaxf(sMargin[0], sMargin[1]), fmaxf(sMargin[2], sMargin[3]));
+        const float dm = fmaxf(fmaxf(sMargin[j & 1][0], sMargin[j & 1][1]),
+                               fmaxf(sMargin[j & 1][2], sMargin[j & 1][3]));
         p.tile_margin[unit_tiles + j] = dm * kLn2;
       }
     }
+    return keep;
+  };
 
-    if (keep) {
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      float psum = 0.f;
-      bf16x8_t pf[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = exp2_fast(fmaf(sacc[kb][i], p.scale_log2, -m_use));
-          psum += pv;
-          pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv;
-        }
-      }
-      l_part = fmaf(l_part, alpha, psum);
+  // Online-softmax update for a kept tile whose running max (through the tile) is m_tile: bring
+  // O and l to the new reference max. Only when some row of the wave got a new maximum;
+  // otherwise alpha is exactly 1.
+  auto rescale_to = [&](float m_tile) {
+    if (__ballot(m_tile > m_ref) != 0ull) {
+      const float alpha = exp2_fast(m_ref - ((m_tile == -INFINITY) ? 0.f : m_tile));
+      l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-      m_run = m_new;
-      const char *vl = smem[st][1];
+    }
+    m_ref = m_tile;
+  };
+
+  // P = exp2(S - m_tile) for a kept tile, as the bf16 B operands of the P V MFMAs.
+  auto exp_p = [&](const f32x16_t *sacc, float m_tile, bf16x8_t *pf) {
+    const float m_use = (m_tile == -INFINITY) ? 0.f : m_tile;
+    float psum = 0.f;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int coff = 16 * ((4 * db + v_cb) ^ v_swz) + v_byte;
-          const char *p0 = vl + 16 * s * RB + v_rowoff + coff;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p0 + 8 * RB));
-          const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s], oacc[db], 0, 0, 0);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const float pv = exp2_fast(fmaf(sacc[kb][i], p.scale_log2, -m_use));
+        psum += pv;
+        pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv;
       }
     }
+    l_part += psum;
+  };
+
+  // O += P V with V in V stage st.
+  auto pv = [&](const bf16x8_t *pf, int st) {
+    const char *vl = smem[st][1];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int coff = 16 * ((4 * db + v_cb) ^ v_swz) + v_byte;
+        const char *p0 = vl + 16 * s * RB + v_rowoff + coff;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p0 + 8 * RB));
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s], oacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // Software pipeline, one barrier per tile. Iteration j: the barrier publishes K_j, V_{j-1}
+  // and the votes for tile j-1; the wave then scores tile j on the matrix cores while (if tile
+  // j-1 is kept) it exponentiates tile j-1 and accumulates P_{j-1} V_{j-1}; finally it votes on
+  // tile j. K_{j+1} and V_j are loaded meanwhile (two LDS stages each).
+  f32x16_t scur[2], sprev[2];
+  issue_k(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (n_tiles > 1) issue_k(1, 1);
+  issue_v(0, 0);
+  compute_s(0, scur);
+  mask_tile(0, scur);
+  publish_margin(0, vote_tile(0, scur));
+  for (int j = 1; j < n_tiles; ++j) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K_j and V_{j-1} have landed
+    __syncthreads();                // ... and every wave's; votes for tile j-1 are visible
+    if (j + 1 < n_tiles) issue_k(j + 1, (j + 1) & 1);
+    issue_v(j, j & 1);
+    const int keep_prev = decision(j - 1);
+    sprev[0] = scur[0];
+    sprev[1] = scur[1];
+    const float m_prev = m_run;
+    compute_s(j & 1, scur);
+    mask_tile(j, scur);
+    if (keep_prev) {
+      rescale_to(m_prev);
+      bf16x8_t pf[4];
+      exp_p(sprev, m_prev, pf);
+      pv(pf, (j - 1) & 1);
+    }
+    publish_margin(j, vote_tile(j, scur));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (decision(n_tiles - 1)) {
+    rescale_to(m_run);
+    bf16x8_t pf[4];
+    exp_p(scur, m_run, pf);
+    pv(pf, (n_tiles - 1) & 1);
   }
 
   // ---- Epilogue: O = acc / l, LSE = m + log l (natural log on output).
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float l_tot = sum_halves(l_part);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __bf16 *orow = (__bf16 *)p.o + b * p.o_sb + (int64_t)my_row * p.o_ss + hq * p.o_sh;
