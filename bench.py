@@ -39,6 +39,8 @@ PREFILL = dict(B=1, Hq=32, Hkv=8, L=8192, d=128, cluster_len=256, sinks=64, seed
 PREFILL_BETA = 32.0   # centre gain giving ~60 % skipped tiles (1.0 = recipe read literally)
 DECODE = dict(B=64, Hq=32, Hkv=8, L=32768, d=128, cluster_len=512, seed=3000)
 DECODE_BETA = 16.0
+MLA = dict(B=32, Hq=128, L=65536, cluster_len=1024, seed=5000)
+MLA_BETA = 16.0
 
 
 def _parse():
@@ -254,6 +256,41 @@ def main():
         out["decode_gqa"] = {"workload": "GQA decode B64 Hq32/Hkv8 KV32768 d128 bf16, "
                                          f"centre gain {DECODE_BETA}", "points": dec}
         del qd, kd, vd
+
+        # MLA-shaped decode: V is the first 512 columns of K, so the bytes are K only.
+        M = MLA
+        qm, km, vm, kvm = decode_inputs(B=M["B"], Hq=M["Hq"], Hkv=1, L=M["L"], d_qk=576,
+                                        d_v=512, cluster_len=M["cluster_len"],
+                                        dtype=torch.bfloat16, device=dev, seed=M["seed"],
+                                        beta=MLA_BETA, share=True, v_aliases_k=True)
+        om = torch.empty((M["B"], M["Hq"], 512), dtype=torch.bfloat16, device=dev)
+        brm, bcm, sm = F.blasst_decode_plan(qm, km, vm)
+        wsm = torch.empty(max(F.blasst_decode_workspace_size(qm, km, vm), 1), dtype=torch.uint8,
+                          device=dev)
+        mla_bytes = M["B"] * M["L"] * 576 * 2 + qm.numel() * 2 + om.numel() * 2
+        mla = []
+        msm0 = None
+        for a in (0.0, 4.0, 16.0, 64.0):
+            la = a / M["L"]
+            fn = lambda la=la: F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om,  # noqa: E731
+                                                    workspace=wsm, stream=stream)
+            msm = _time_calls(fn, args.steps, args.warmup, stream)
+            cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+            F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om, counters=cnt, workspace=wsm)
+            torch.cuda.synchronize()
+            vis, sk = (int(x) for x in cnt.cpu().tolist())
+            if a == 0.0:
+                msm0 = msm
+            flops = 2.0 * 64 * 64 * (576 * vis + 512 * (vis - sk)) * 1.0
+            mla.append({"lambda": f"{int(a)}/L", "ms": msm, "skip_fraction": sk / max(vis, 1),
+                        "GB/s": mla_bytes / (msm * 1e-3) / 1e9,
+                        "hbm_frac": mla_bytes / (msm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "executed_tflops": flops / (msm * 1e-3) / 1e12,
+                        "speedup_vs_lambda0": msm0 / msm})
+        out["decode_mla"] = {"workload": "MLA-shaped decode B32 Hq128 KV65536 d_qk576/d_v512 bf16, "
+                                         f"centre gain {MLA_BETA}, tile {brm}x{bcm}, "
+                                         f"{sm} splits", "points": mla}
+        del qm, km, vm
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(q, k, v, lam, br, bc)

@@ -216,7 +216,7 @@ blasst_status blasst_decode_plan(const blasst_decode_args *a, int32_t *block_r, 
     if (br < 1 || br > 16) return BLASST_ERR_UNSUPPORTED;
   } else {
     br = a->block_r ? a->block_r : 64;
-    if (br != 64 && br != 128) return BLASST_ERR_UNSUPPORTED;
+    if (br != 64) return BLASST_ERR_UNSUPPORTED;
   }
   if (br > group) br = group;
   const int n_tiles = ceil_div(a->max_kv_len, bc);

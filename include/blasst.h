@@ -174,7 +174,7 @@ blasst_status blasst_prefill_tiles(const blasst_prefill_args *args, int32_t *blo
  *
  * Supported: BLASST_BF16; GQA kernel: head_dim_qk == head_dim_v == 128 (or 64), block_c 64,
  * block_r <= 16; MLA kernel: head_dim_qk 576, head_dim_v 512, heads_kv 1, v == k, block_c 64,
- * block_r 64 (default) or 128. tile_status / tile_margin:
+ * block_r 64. tile_status / tile_margin:
  * [batch, heads_kv, ceil(G / block_r), ceil(max_kv_len / block_c)], G = heads_q / heads_kv.
  * ------------------------------------------------------------------------------------------ */
 typedef struct blasst_decode_args {

@@ -1,7 +1,8 @@
 """Shared comparison rules for GPU-vs-oracle parity tests.
 
-Bar (bf16 inputs, fp32 accumulation): max|dO| <= 1e-2 * max|O| and mean|dO| <= 1e-3 over the
-compared outputs; LSE within 1e-2 (natural log). fp32 inputs: max|dO| <= 1e-4 * max|O|,
+Bar (bf16 inputs, fp32 accumulation): max|dO| <= 1e-2 * max|O| against the exact oracle and
+mean|dO| <= 1e-3 against the oracle rounded to the output dtype (bf16 rounding of an output of
+magnitude ~1 alone is ~1e-3 on average); LSE within 1e-2 (natural log). fp32 inputs: max|dO| <= 1e-4 * max|O|,
 mean|dO| <= 1e-5, LSE within 1e-4. Skip decisions must agree exactly on every tile whose oracle
 margin lies outside a band around ln(lambda); inside the band float rounding may flip the
 decision, and such tiles are counted, not failed (their units are then compared against the
@@ -31,15 +32,22 @@ def tau(lam: float) -> float:
     return -math.inf if lam == 0 else math.log(min(lam, 1.0))
 
 
+def _round_to(x: np.ndarray, dtype) -> np.ndarray:
+    return torch.as_tensor(x, dtype=torch.float64).to(dtype).to(torch.float64).numpy()
+
+
 def assert_outputs_close(o_gpu: np.ndarray, o_ref: np.ndarray, dtype, what: str):
+    """max|dO| against the exact oracle; mean|dO| against the oracle rounded to the output dtype
+    (a bf16 output of magnitude ~1 carries ~1e-3 of rounding on its own, whatever computed it)."""
     tol = TOL[dtype]
     err = np.abs(o_gpu - o_ref)
     scale = np.abs(o_ref).max()
     assert np.isfinite(o_gpu).all(), f"{what}: non-finite output"
     assert err.max() <= tol["max_rel"] * scale, \
         f"{what}: max|dO| {err.max():.3e} > {tol['max_rel']} * max|O| ({scale:.3e})"
-    assert err.mean() <= tol["mean_abs"], f"{what}: mean|dO| {err.mean():.3e}"
-    return float(err.max()), float(err.mean())
+    mean_err = np.abs(o_gpu - _round_to(o_ref, dtype)).mean()
+    assert mean_err <= tol["mean_abs"], f"{what}: mean|dO| {mean_err:.3e} (vs rounded oracle)"
+    return float(err.max()), float(mean_err)
 
 
 def assert_lse_close(lse_gpu: np.ndarray, lse_ref: np.ndarray, dtype, what: str):

@@ -144,3 +144,35 @@ def test_gqa_decode_full_size_sampled():
         assert res["counters"][0] == int((st != 2).sum())
         assert res["counters"][1] == int((st == 1).sum())
         assert ref.skipped > 0
+
+
+def test_mla_small_lengths_and_splits():
+    """MLA shape: 128 query heads on one latent KV head, d_qk 576, V = the first 512 columns."""
+    L = 700
+    lams = [0.0, 16 / L, 1.0]
+    _case(2, 128, 1, L, 576, [700, 321], lams[:2], (1, 3), 1.0, True, seed=31, Dv=512,
+          cluster_len=128)
+    assert _case(2, 128, 1, L, 576, [700, 130], lams, (1, 4), 16.0, True, seed=32, Dv=512,
+                 cluster_len=128) > 0
+
+
+def test_mla_decode_full_size_sampled():
+    """MLA-shaped decode at full size: 32 sequences x 128 heads, KV 65536, d_qk 576 / d_v 512."""
+    need_gpu()
+    B, Hq, L = 32, 128, 65536
+    q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=1, L=L, d_qk=576, d_v=512, cluster_len=1024,
+                                 dtype=torch.bfloat16, device="cuda", seed=5000, beta=16.0,
+                                 share=True, v_aliases_k=True)
+    units = [(0, 0, 0), (31, 0, 1), (7, 0, 0), (19, 0, 1)]
+    for a in (4, 64):
+        lam = a / L
+        what = f"MLA lam={a}/L"
+        print(what, flush=True)
+        res = _run_gpu(q, k, v, kvl, lam=lam)
+        ref = oracle.decode(q, k, v, kv_len=kvl, block_r=res["br"], block_c=res["bc"],
+                            num_splits=res["splits"], scale=oracle_scale(576), lam=lam,
+                            units=units, threads=16)
+        _check(res, ref, q, k, v, lam, what, kvl)
+        st = res["status"]
+        assert res["counters"][0] == int((st != 2).sum())
+        assert res["counters"][1] == int((st == 1).sum())
