@@ -15,7 +15,10 @@ Secondary measurements (same line): lambda = 0 on the same kernel and data (spee
 two thresholds, the literal generator (centre gain 1, nothing skipped), and GQA decode
 (64 x 32/8 heads, KV 32768, d 128) in GB/s against HBM.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                      [--part all|prefill|decode|mla] [--a A]
+       python bench.py --copy-calibration BYTES       (reference copy for counter scaling)
+       python bench.py --counter-summary ...          (no GPU: rocprofv3 CSV -> profiles/*.json)
 """
 from __future__ import annotations
 
@@ -46,14 +49,33 @@ MLA_BETA = 16.0
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
+    ap.add_argument("--quick", action="store_true", help="same as --part prefill")
+    ap.add_argument("--part", choices=("all", "prefill", "decode", "mla"), default="all",
+                    help="prefill: the headline call only; decode / mla: that decode only "
+                         "(profiling runs isolate one kernel this way)")
+    ap.add_argument("--a", type=float, default=None,
+                    help="decode parts: time only lambda = a / L instead of the sweep")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes three times "
                          "(the reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
-    return ap.parse_args()
+    ap.add_argument("--counter-summary", nargs=6, default=None,
+                    metavar=("OUT_JSON", "KERNEL", "SOURCE", "FETCH_DIR", "WRITE_DIR", "COPY_DIRS"),
+                    help="no GPU: summarise rocprofv3 --pmc CSV output into OUT_JSON for the "
+                         "kernel whose name contains KERNEL, built from csrc/SOURCE; COPY_DIRS is "
+                         "'FETCH_COPY_DIR,WRITE_COPY_DIR' from the --copy-calibration runs")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--commands", default="", help="with --counter-summary: the commands, recorded")
+    args = ap.parse_args()
+    if args.quick:
+        args.part = "prefill"
+    return args
+
+
+def _progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def _time_calls(fn, steps, warmup, stream):
@@ -133,28 +155,68 @@ def _cpu_baseline(q, k, v, lam, br, bc, budget_s=12.0):
                        f"{elapsed:.1f} s wall, fp64")
 
 
-def main():
-    args = _parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is a design note, not built)"}))
-        sys.exit(2)
-    import torch
+def _counter_csv(d):
+    """Rows of the counter_collection CSV that rocprofv3 --output-format csv wrote under d."""
+    import csv
+    import glob
 
-    if args.copy_calibration:
-        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": args.copy_calibration, "copies": 3}))
-        return
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
 
-    import flashattention_softmax_threshold_amd as F
-    from flashattention_softmax_threshold_amd.inputs import decode_inputs, prefill_inputs
 
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
+def _counter_mean(d, kernel, counter):
+    """Mean over dispatches of `counter` (summed over its instances) for kernels matching."""
+    per_dispatch = {}
+    for r in _counter_csv(d):
+        if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    if not per_dispatch:
+        raise SystemExit(f"{counter} for '{kernel}' not found under {d}")
+    vals = list(per_dispatch.values())
+    return sum(vals) / len(vals), len(vals)
+
+
+def _write_counter_summary(args):
+    out_json, kernel, source, fdir, wdir, copy_dirs = args.counter_summary
+    fcopy, wcopy = copy_dirs.split(",")
+    fetch_kib, nf = _counter_mean(fdir, kernel, "FETCH_SIZE")
+    write_kib, nw = _counter_mean(wdir, kernel, "WRITE_SIZE")
+    # The copy kernel of --copy-calibration reads and writes copy_bytes per dispatch.
+    cf_kib, _ = _counter_mean(fcopy, "copyBuffer", "FETCH_SIZE")
+    cw_kib, _ = _counter_mean(wcopy, "copyBuffer", "WRITE_SIZE")
+    fetch_factor = args.copy_bytes / 1024.0 / cf_kib
+    write_factor = args.copy_bytes / 1024.0 / cw_kib
+    rec = {
+        "kernel": kernel,
+        "kernel_source": source,
+        "kernel_source_sha256_16": _kernel_source_hash(source),
+        "dispatches": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
+        "fetch_size_kib_per_dispatch": fetch_kib,
+        "write_size_kib_per_dispatch": write_kib,
+        "copy_calibration": {"bytes": args.copy_bytes, "fetch_size_kib": cf_kib,
+                             "write_size_kib": cw_kib, "fetch_factor": fetch_factor,
+                             "write_factor": write_factor},
+        "hbm_read_bytes_per_launch": fetch_kib * 1024.0 * fetch_factor,
+        "hbm_write_bytes_per_launch": write_kib * 1024.0 * write_factor,
+        "hbm_bytes_per_launch": fetch_kib * 1024.0 * fetch_factor + write_kib * 1024.0 * write_factor,
+        "commands": args.commands,
+    }
+    with open(out_json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+
+
+def _prefill_part(F, torch, args, dev, stream, out):
+    from flashattention_softmax_threshold_amd.inputs import prefill_inputs
+
     P = PREFILL
     L, d, Hq = P["L"], P["d"], P["Hq"]
     dense_flops = 4.0 * Hq * d * L * (L + 1) / 2
@@ -174,19 +236,12 @@ def main():
     kept = visited - skipped
     exec_flops = tile_flops * (visited + kept)
     achieved = exec_flops / (ms * 1e-3) / 1e12
-    traffic = _traffic_from_profile("prefill.hip", "prefill_c2_counters.json")
-    out = {
-        "metric": "attention TFLOP/s (dense-equiv) + % MFMA peak; decode GB/s; skip fraction",
+    _progress(f"prefill headline: {ms:.4f} ms, skip {skipped / visited:.3f}, "
+              f"{achieved:.0f} executed TFLOP/s")
+    traffic = _traffic_from_profile("prefill_mfma.hip", "prefill_mfma_c2_counters.json")
+    out.update({
         "value": dense_flops / (ms * 1e-3) / 1e12,
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
         "data": f"synthetic clustered (256-token clusters, 64 sink keys, centre gain {PREFILL_BETA})",
         "config": {"workload": "causal GQA prefill B1 Hq32/Hkv8 L8192 d128 bf16, tile 128x64, "
                                "lambda=16/L", "batch": 1, "seq_len": L, "heads_q": Hq,
@@ -197,9 +252,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
                      "traffic": traffic},
-    }
+    })
 
-    if not args.quick:
+    if args.part == "all":
         # Same kernel, same data: lambda = 0 and the other thresholds.
         ms0 = _time_calls(prefill_step(0.0), args.steps, args.warmup, stream)
         v0, _ = _prefill_counts(F, q, k, v, 0.0)
@@ -215,6 +270,7 @@ def main():
         out["prefill_lambda0"] = {"ms": ms0, "dense_tflops": dense_flops / (ms0 * 1e-3) / 1e12,
                                   "executed_tflops": tile_flops * 2 * v0 / (ms0 * 1e-3) / 1e12}
         out["prefill_sweep"] = sweep
+        _progress("prefill sweep done")
         # The recipe read literally (centre gain 1): nothing is skipped; overhead of the test.
         q1, k1, v1 = prefill_inputs(B=P["B"], L=L, Hq=Hq, Hkv=P["Hkv"], d=d,
                                     cluster_len=P["cluster_len"], dtype=torch.bfloat16,
@@ -226,73 +282,139 @@ def main():
                                         "skip_fraction": s1c / v1c,
                                         "speedup_vs_lambda0": ms10 / ms1}
         del q1, k1, v1
+        _progress("prefill centre gain 1 done")
+    return q, k, v, lam, br, bc
 
-        # GQA decode.
-        D = DECODE
-        qd, kd, vd, kvl = decode_inputs(B=D["B"], Hq=D["Hq"], Hkv=D["Hkv"], L=D["L"], d_qk=D["d"],
-                                        d_v=D["d"], cluster_len=D["cluster_len"],
-                                        dtype=torch.bfloat16, device=dev, seed=D["seed"],
-                                        beta=DECODE_BETA)
-        od = torch.empty((D["B"], D["Hq"], D["d"]), dtype=torch.bfloat16, device=dev)
-        tile_bytes = 64 * D["d"] * 2
-        dec = []
-        msd0 = None
-        for a in (0.0, 4.0, 16.0, 64.0):
-            la = a / D["L"]
-            fn = lambda la=la: F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od,  # noqa: E731
-                                                    stream=stream)
-            msd = _time_calls(fn, args.steps, args.warmup, stream)
-            cnt = torch.zeros(2, dtype=torch.int64, device=dev)
-            F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od, counters=cnt)
-            torch.cuda.synchronize()
-            vis, sk = (int(x) for x in cnt.cpu().tolist())
-            nbytes = tile_bytes * (2 * vis - sk) + qd.numel() * 2 + od.numel() * 2
-            if a == 0.0:
-                msd0 = msd
-            dec.append({"lambda": f"{int(a)}/L", "ms": msd, "skip_fraction": sk / max(vis, 1),
-                        "GB/s": nbytes / (msd * 1e-3) / 1e9,
-                        "hbm_frac": nbytes / (msd * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                        "speedup_vs_lambda0": msd0 / msd})
-        out["decode_gqa"] = {"workload": "GQA decode B64 Hq32/Hkv8 KV32768 d128 bf16, "
-                                         f"centre gain {DECODE_BETA}", "points": dec}
-        del qd, kd, vd
 
-        # MLA-shaped decode: V is the first 512 columns of K, so the bytes are K only.
-        M = MLA
-        qm, km, vm, kvm = decode_inputs(B=M["B"], Hq=M["Hq"], Hkv=1, L=M["L"], d_qk=576,
-                                        d_v=512, cluster_len=M["cluster_len"],
-                                        dtype=torch.bfloat16, device=dev, seed=M["seed"],
-                                        beta=MLA_BETA, share=True, v_aliases_k=True)
-        om = torch.empty((M["B"], M["Hq"], 512), dtype=torch.bfloat16, device=dev)
-        brm, bcm, sm = F.blasst_decode_plan(qm, km, vm)
-        wsm = torch.empty(max(F.blasst_decode_workspace_size(qm, km, vm), 1), dtype=torch.uint8,
-                          device=dev)
-        mla_bytes = M["B"] * M["L"] * 576 * 2 + qm.numel() * 2 + om.numel() * 2
-        mla = []
-        msm0 = None
-        for a in (0.0, 4.0, 16.0, 64.0):
-            la = a / M["L"]
-            fn = lambda la=la: F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om,  # noqa: E731
-                                                    workspace=wsm, stream=stream)
-            msm = _time_calls(fn, args.steps, args.warmup, stream)
-            cnt = torch.zeros(2, dtype=torch.int64, device=dev)
-            F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om, counters=cnt, workspace=wsm)
-            torch.cuda.synchronize()
-            vis, sk = (int(x) for x in cnt.cpu().tolist())
-            if a == 0.0:
-                msm0 = msm
-            flops = 2.0 * 64 * 64 * (576 * vis + 512 * (vis - sk)) * 1.0
-            mla.append({"lambda": f"{int(a)}/L", "ms": msm, "skip_fraction": sk / max(vis, 1),
-                        "GB/s": mla_bytes / (msm * 1e-3) / 1e9,
-                        "hbm_frac": mla_bytes / (msm * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                        "executed_tflops": flops / (msm * 1e-3) / 1e12,
-                        "speedup_vs_lambda0": msm0 / msm})
-        out["decode_mla"] = {"workload": "MLA-shaped decode B32 Hq128 KV65536 d_qk576/d_v512 bf16, "
-                                         f"centre gain {MLA_BETA}, tile {brm}x{bcm}, "
-                                         f"{sm} splits", "points": mla}
-        del qm, km, vm
+def _sweep_points(args):
+    return (0.0, 4.0, 16.0, 64.0) if args.a is None else (args.a,)
 
-    if not args.no_cpu_baseline:
+
+def _decode_part(F, torch, args, dev, stream, out):
+    from flashattention_softmax_threshold_amd.inputs import decode_inputs
+
+    D = DECODE
+    qd, kd, vd, kvl = decode_inputs(B=D["B"], Hq=D["Hq"], Hkv=D["Hkv"], L=D["L"], d_qk=D["d"],
+                                    d_v=D["d"], cluster_len=D["cluster_len"],
+                                    dtype=torch.bfloat16, device=dev, seed=D["seed"],
+                                    beta=DECODE_BETA)
+    od = torch.empty((D["B"], D["Hq"], D["d"]), dtype=torch.bfloat16, device=dev)
+    brd, bcd, sd = F.blasst_decode_plan(qd, kd, vd)
+    wsd = torch.empty(max(F.blasst_decode_workspace_size(qd, kd, vd), 1), dtype=torch.uint8,
+                      device=dev)
+    tile_bytes = bcd * D["d"] * 2
+    dec = []
+    msd0 = None
+    for a in _sweep_points(args):
+        la = a / D["L"]
+        fn = lambda la=la: F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od,  # noqa: E731
+                                                workspace=wsd, stream=stream)
+        msd = _time_calls(fn, args.steps, args.warmup, stream)
+        cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+        F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od, counters=cnt, workspace=wsd)
+        torch.cuda.synchronize()
+        vis, sk = (int(x) for x in cnt.cpu().tolist())
+        # Algorithmic bytes: K of every visited tile, V of every kept tile, Q in, O out.
+        nbytes = tile_bytes * (2 * vis - sk) + qd.numel() * 2 + od.numel() * 2
+        if a == 0.0:
+            msd0 = msd
+        dec.append({"lambda": f"{a:g}/L", "ms": msd, "skip_fraction": sk / max(vis, 1),
+                    "GB/s": nbytes / (msd * 1e-3) / 1e9,
+                    "hbm_frac": nbytes / (msd * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "speedup_vs_lambda0": (msd0 / msd) if msd0 else None})
+        _progress(f"decode gqa a={a:g}: {msd:.4f} ms")
+    out["decode_gqa"] = {"workload": "GQA decode B64 Hq32/Hkv8 KV32768 d128 bf16, "
+                                     f"centre gain {DECODE_BETA}, tile {brd}x{bcd}, {sd} splits",
+                         "points": dec}
+
+
+def _mla_part(F, torch, args, dev, stream, out):
+    # MLA-shaped decode: V is the first 512 columns of K, so the bytes are K only.
+    from flashattention_softmax_threshold_amd.inputs import decode_inputs
+
+    M = MLA
+    qm, km, vm, kvm = decode_inputs(B=M["B"], Hq=M["Hq"], Hkv=1, L=M["L"], d_qk=576,
+                                    d_v=512, cluster_len=M["cluster_len"],
+                                    dtype=torch.bfloat16, device=dev, seed=M["seed"],
+                                    beta=MLA_BETA, share=True, v_aliases_k=True)
+    om = torch.empty((M["B"], M["Hq"], 512), dtype=torch.bfloat16, device=dev)
+    brm, bcm, sm = F.blasst_decode_plan(qm, km, vm)
+    wsm = torch.empty(max(F.blasst_decode_workspace_size(qm, km, vm), 1), dtype=torch.uint8,
+                      device=dev)
+    mla_bytes = M["B"] * M["L"] * 576 * 2 + qm.numel() * 2 + om.numel() * 2
+    mla = []
+    msm0 = None
+    for a in _sweep_points(args):
+        la = a / M["L"]
+        fn = lambda la=la: F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om,  # noqa: E731
+                                                workspace=wsm, stream=stream)
+        msm = _time_calls(fn, args.steps, args.warmup, stream)
+        cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+        F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om, counters=cnt, workspace=wsm)
+        torch.cuda.synchronize()
+        vis, sk = (int(x) for x in cnt.cpu().tolist())
+        if a == 0.0:
+            msm0 = msm
+        # Executed MFMA work per visited tile: B_r x B_c x 576 for S, per kept tile x 512 for PV.
+        flops = 2.0 * brm * bcm * (576 * vis + 512 * (vis - sk))
+        mla.append({"lambda": f"{a:g}/L", "ms": msm, "skip_fraction": sk / max(vis, 1),
+                    "GB/s": mla_bytes / (msm * 1e-3) / 1e9,
+                    "hbm_frac": mla_bytes / (msm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "executed_tflops": flops / (msm * 1e-3) / 1e12,
+                    "speedup_vs_lambda0": (msm0 / msm) if msm0 else None})
+        _progress(f"decode mla a={a:g}: {msm:.4f} ms")
+    out["decode_mla"] = {"workload": "MLA-shaped decode B32 Hq128 KV65536 d_qk576/d_v512 bf16, "
+                                     f"centre gain {MLA_BETA}, tile {brm}x{bcm}, {sm} splits",
+                         "points": mla}
+
+
+def main():
+    args = _parse()
+    if args.counter_summary:
+        _write_counter_summary(args)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is a design note, not built)"}))
+        sys.exit(2)
+    import torch
+
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calibration, "copies": 3}))
+        return
+
+    import flashattention_softmax_threshold_amd as F
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    out = {
+        "metric": "attention TFLOP/s (dense-equiv) + % MFMA peak; decode GB/s; skip fraction",
+        "value": None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+    }
+    headline = None
+    if args.part in ("all", "prefill"):
+        headline = _prefill_part(F, torch, args, dev, stream, out)
+    if args.part in ("all", "decode"):
+        _decode_part(F, torch, args, dev, stream, out)
+    if args.part in ("all", "mla"):
+        _mla_part(F, torch, args, dev, stream, out)
+    if headline is not None and not args.no_cpu_baseline:
+        q, k, v, lam, br, bc = headline
+        _progress("cpu baseline (oracle, about 12 s)")
         out["cpu_baseline"] = _cpu_baseline(q, k, v, lam, br, bc)
     print(json.dumps(out), flush=True)
 
