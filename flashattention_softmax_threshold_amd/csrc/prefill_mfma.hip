@@ -60,16 +60,58 @@ __device__ __forceinline__ float sum_halves(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Max of the 32 scores a lane holds, as a shallow tree.
+// Max of the 32 scores a lane holds: a tree of three-input maxima (v_max3_f32), 16 VALU ops.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 __device__ __forceinline__ float max32(const f32x16_t &a, const f32x16_t &b) {
-  float m[8];
+  float m[11];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) m[i] = max3f(a[3 * i], a[3 * i + 1], a[3 * i + 2]);
+#pragma unroll
+  for (int i = 0; i < 5; ++i) m[5 + i] = max3f(b[3 * i], b[3 * i + 1], b[3 * i + 2]);
+  m[10] = fmaxf(a[15], b[15]);
+  const float x = max3f(m[0], m[1], m[2]), y = max3f(m[3], m[4], m[5]);
+  const float z = max3f(m[6], m[7], m[8]);
+  return max3f(max3f(x, y, z), m[9], m[10]);
+}
+
+// Sum of the 32 bf16 P values of a lane, two per v_dot2_f32_bf16 against (1, 1): the row sum is
+// taken over exactly the rounded P that enters the P V product.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float sum_p(const bf16x8_t *pf) {
+  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+  float s0 = 0.f, s1 = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    m[i] = fmaxf(fmaxf(a[4 * i], a[4 * i + 1]), fmaxf(a[4 * i + 2], a[4 * i + 3]));
-    m[4 + i] = fmaxf(fmaxf(b[4 * i], b[4 * i + 1]), fmaxf(b[4 * i + 2], b[4 * i + 3]));
+    const bf16x2_t x0 = {pf[i][0], pf[i][1]}, x1 = {pf[i][2], pf[i][3]};
+    const bf16x2_t x2 = {pf[i][4], pf[i][5]}, x3 = {pf[i][6], pf[i][7]};
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(x0, one, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(x1, one, s1, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(x2, one, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, s1, false);
   }
-  return fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])),
-               fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
+  return s0 + s1;
+}
+
+// O and l are rescaled only when some row's max has grown by more than this (base-2 units)
+// since the last rescale: P = 2^(s - m_ref) then stays below 2^8, and the algebra is exact.
+constexpr float kRescaleSlack = 8.f;
+
+
+// HBM -> LDS copies issued as inline assembly. The compiler does not see them as LDS writes, so
+// it adds no conservative "wait for every load" in front of LDS reads of the other pipeline
+// stages; the kernel's own s_waitcnt + barrier at the top of each step orders the data. M0 holds
+// the wave's LDS destination (lane i lands at M0 + size * i); nothing else in this kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved to the compiler; see above
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
 template <int D>
@@ -156,8 +198,7 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
 #pragma unroll
       for (int t2 = 0; t2 < G::LOADS_PER_WAVE; ++t2) {
         const int ii = wv * G::LOADS_PER_WAVE + t2;
-        __builtin_amdgcn_global_load_lds((const void *)(tb + (op ? v_off[t2] : k_off[t2])),
-                                         (lds_void_t *)(&smem[st][op][ii * 1024]), 16, 0, 0);
+        lds_dma16(tb + (op ? v_off[t2] : k_off[t2]), lds_addr(&smem[st][op][ii * 1024]));
       }
     } else {
 #pragma unroll
@@ -167,8 +208,7 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
         const int key = min(k0 + r, p.Lkv - 1);
         const int sw = op ? swz_v(r, CPR) : swz_k(r, CPR);
         const __bf16 *gp = base + (int64_t)key * ss + 8 * (ld_pc ^ sw);
-        __builtin_amdgcn_global_load_lds((const void *)gp,
-                                         (lds_void_t *)(&smem[st][op][ii * 1024]), 16, 0, 0);
+        lds_dma16(gp, lds_addr(&smem[st][op][ii * 1024]));
       }
     }
   };
@@ -264,14 +304,16 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
   // Optional observation: the wave's largest row margin for tile j.
   auto publish_margin = [&](int j, float dm) {
     if (p.tile_margin) {
+      asm volatile("" : "+v"(dm));  // keeps the reduction inside the branch (no speculation)
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) dm = fmaxf(dm, __shfl_xor(dm, o));
       sMargin[j & 1][wv] = dm;
     }
   };
 
-  auto decision = [&](int j) {
-    const int keep = sVote[j & 1][0] | sVote[j & 1][1] | sVote[j & 1][2] | sVote[j & 1][3];
+  auto read_votes = [&](int j) { return *(const int4 *)&sVote[j & 1][0]; };
+  auto decision = [&](int j, int4 vt) {
+    const int keep = vt.x | vt.y | vt.z | vt.w;
     if (tid == 0) {
       ++visited;
       skipped += keep ? 0u : 1u;
@@ -285,33 +327,29 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
     return keep;
   };
 
-  // Online-softmax update for a kept tile whose running max (through the tile) is m_tile: bring
-  // O and l to the new reference max. Only when some row of the wave got a new maximum;
-  // otherwise alpha is exactly 1.
+  // Online-softmax update for a kept tile whose running max (through the tile) is m_tile. O and
+  // l stay scaled to m_ref until some row of the wave exceeds it by more than kRescaleSlack;
+  // then every row of the wave moves to its own m_tile.
   auto rescale_to = [&](float m_tile) {
-    if (__ballot(m_tile > m_ref) != 0ull) {
+    if (__ballot(m_tile > m_ref + kRescaleSlack) != 0ull) {
       const float alpha = exp2_fast(m_ref - ((m_tile == -INFINITY) ? 0.f : m_tile));
       l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+      m_ref = m_tile;
     }
-    m_ref = m_tile;
   };
 
-  // P = exp2(S - m_tile) for a kept tile, as the bf16 B operands of the P V MFMAs.
-  auto exp_p = [&](const f32x16_t *sacc, float m_tile, bf16x8_t *pf) {
-    const float m_use = (m_tile == -INFINITY) ? 0.f : m_tile;
-    float psum = 0.f;
+  // P = exp2(S - m_ref) for a kept tile, as the bf16 B operands of the P V MFMAs.
+  auto exp_p = [&](const f32x16_t *sacc, bf16x8_t *pf) {
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = exp2_fast(fmaf(sacc[kb][i], p.scale_log2, -m_use));
-        psum += pv;
-        pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv;
-      }
+      for (int i = 0; i < 16; ++i)
+        pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)exp2_fast(fmaf(sacc[kb][i], p.scale_log2, -m_use));
     }
-    l_part += psum;
+    l_part += sum_p(pf);
   };
 
   // O += P V with V in V stage st.
@@ -332,45 +370,58 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
     }
   };
 
-  // Software pipeline, one barrier per tile. Iteration j: the barrier publishes K_j, V_{j-1}
-  // and the votes for tile j-1; the wave then scores tile j on the matrix cores while (if tile
-  // j-1 is kept) it exponentiates tile j-1 and accumulates P_{j-1} V_{j-1}; finally it votes on
-  // tile j. K_{j+1} and V_j are loaded meanwhile (two LDS stages each).
-  f32x16_t scur[2], sprev[2];
+  // Software pipeline, one barrier per tile. Step j: the barrier publishes K_j, V_{j-1} and the
+  // votes for tile j-1; the wave then scores tile j on the matrix cores while (if tile j-1 is
+  // kept) it exponentiates tile j-1 and accumulates P_{j-1} V_{j-1}; finally it votes on tile j.
+  // K_{j+1} and V_j are loaded meanwhile (two LDS stages each). The scores alternate between two
+  // register sets, so no step copies them.
+  auto step = [&](int j, f32x16_t *cur, const f32x16_t *prev) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's K_j and V_{j-1} have landed
+    __syncthreads();                // ... and every wave's; votes for tile j-1 are visible
+    const int4 vt = read_votes(j - 1);
+    if (j + 1 < n_tiles) issue_k(j + 1, (j + 1) & 1);
+    issue_v(j, j & 1);
+    const int keep_prev = decision(j - 1, vt);
+    const float m_prev = m_run;
+    compute_s(j & 1, cur);
+    mask_tile(j, cur);
+    if (keep_prev) {
+      rescale_to(m_prev);
+      bf16x8_t pf[4];
+      exp_p(prev, pf);
+      pv(pf, (j - 1) & 1);
+    }
+    publish_margin(j, vote_tile(j, cur));
+  };
+  auto finish = [&](const f32x16_t *last) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (decision(n_tiles - 1, read_votes(n_tiles - 1))) {
+      rescale_to(m_run);
+      bf16x8_t pf[4];
+      exp_p(last, pf);
+      pv(pf, (n_tiles - 1) & 1);
+    }
+  };
+  f32x16_t sa[2], sb[2];
   issue_k(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (n_tiles > 1) issue_k(1, 1);
   issue_v(0, 0);
-  compute_s(0, scur);
-  mask_tile(0, scur);
-  publish_margin(0, vote_tile(0, scur));
-  for (int j = 1; j < n_tiles; ++j) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K_j and V_{j-1} have landed
-    __syncthreads();                // ... and every wave's; votes for tile j-1 are visible
-    if (j + 1 < n_tiles) issue_k(j + 1, (j + 1) & 1);
-    issue_v(j, j & 1);
-    const int keep_prev = decision(j - 1);
-    sprev[0] = scur[0];
-    sprev[1] = scur[1];
-    const float m_prev = m_run;
-    compute_s(j & 1, scur);
-    mask_tile(j, scur);
-    if (keep_prev) {
-      rescale_to(m_prev);
-      bf16x8_t pf[4];
-      exp_p(sprev, m_prev, pf);
-      pv(pf, (j - 1) & 1);
-    }
-    publish_margin(j, vote_tile(j, scur));
+  compute_s(0, sa);
+  mask_tile(0, sa);
+  publish_margin(0, vote_tile(0, sa));
+  int j = 1;
+  for (; j + 1 < n_tiles; j += 2) {
+    step(j, sb, sa);
+    step(j + 1, sa, sb);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (decision(n_tiles - 1)) {
-    rescale_to(m_run);
-    bf16x8_t pf[4];
-    exp_p(scur, m_run, pf);
-    pv(pf, (n_tiles - 1) & 1);
+  if (j < n_tiles) {
+    step(j, sb, sa);
+    finish(sb);
+  } else {
+    finish(sa);
   }
 
   // ---- Epilogue: O = acc / l, LSE = m + log l (natural log on output).
@@ -390,7 +441,7 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
     }
     if (p.lse && hh == 0) {
       p.lse[((int64_t)b * p.Hq + hq) * p.Lq + my_row] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+          l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
   if (tid == 0) {
