@@ -74,23 +74,7 @@ __device__ __forceinline__ float max32(const f32x16_t &a, const f32x16_t &b) {
   return max3f(max3f(x, y, z), m[9], m[10]);
 }
 
-// Sum of the 32 bf16 P values of a lane, two per v_dot2_f32_bf16 against (1, 1): the row sum is
-// taken over exactly the rounded P that enters the P V product.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float sum_p(const bf16x8_t *pf) {
-  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x2_t x0 = {pf[i][0], pf[i][1]}, x1 = {pf[i][2], pf[i][3]};
-    const bf16x2_t x2 = {pf[i][4], pf[i][5]}, x3 = {pf[i][6], pf[i][7]};
-    s0 = __builtin_amdgcn_fdot2_f32_bf16(x0, one, s0, false);
-    s1 = __builtin_amdgcn_fdot2_f32_bf16(x1, one, s1, false);
-    s0 = __builtin_amdgcn_fdot2_f32_bf16(x2, one, s0, false);
-    s1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, s1, false);
-  }
-  return s0 + s1;
-}
 
 // O and l are rescaled only when some row's max has grown by more than this (base-2 units)
 // since the last rescale: P = 2^(s - m_ref) then stays below 2^8, and the algebra is exact.
@@ -340,33 +324,64 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
     }
   };
 
-  // P = exp2(S - m_ref) for a kept tile, as the bf16 B operands of the P V MFMAs.
-  auto exp_p = [&](const f32x16_t *sacc, bf16x8_t *pf) {
+  // O += P V for a kept tile: P = exp2(S - m_ref) in bf16 is the B operand of k-step s (keys
+  // 16 s .. 16 s + 15: scores sacc[s / 2][8 (s % 2) ..]); the V^T A operands come from the
+  // row-major V tile in stage st through ds_read_b64_tr_b16. Software-pipelined over the four
+  // k-steps: the V reads of step s + 1 are in flight and the exponentials of step s + 1 are
+  // computed while the MFMAs of step s run.
+  auto exp_pv = [&](const f32x16_t *sacc, int st) {
+    constexpr int NDB = D / 32;        // output column blocks
+    constexpr int NM = 4 * NDB;        // MFMAs: (k-step s, column block db) = (m / NDB, m % NDB)
+    constexpr int RA = 2;              // V operands read this many MFMAs ahead
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)exp2_fast(fmaf(sacc[kb][i], p.scale_log2, -m_use));
-    }
-    l_part += sum_p(pf);
-  };
-
-  // O += P V with V in V stage st.
-  auto pv = [&](const bf16x8_t *pf, int st) {
     const char *vl = smem[st][1];
+    auto rdv = [&](int m) {
+      const int s = m / NDB, db = m % NDB;
+      const int coff = 16 * ((4 * db + v_cb) ^ v_swz) + v_byte;
+      const char *p0 = vl + 16 * s * RB + v_rowoff + coff;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p0 + 8 * RB));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto mkp = [&](int s) {
+      bf16x8_t pk;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int i = 0; i < 8; ++i)
+        pk[i] = (__bf16)exp2_fast(fmaf(sacc[s >> 1][8 * (s & 1) + i], p.scale_log2, -m_use));
+      return pk;
+    };
+    const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+    float ps0 = 0.f, ps1 = 0.f;
+    bf16x8_t va[RA + 1];
+    bf16x8_t pc = mkp(0), pn = pc;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int coff = 16 * ((4 * db + v_cb) ^ v_swz) + v_byte;
-        const char *p0 = vl + 16 * s * RB + v_rowoff + coff;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p0 + 8 * RB));
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s], oacc[db], 0, 0, 0);
+    for (int m = 0; m < RA; ++m) va[m] = rdv(m);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int s = m / NDB, db = m % NDB;
+      if (m + RA < NM) va[(m + RA) % (RA + 1)] = rdv(m + RA);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m % (RA + 1)], pc, oacc[db], 0, 0, 0);
+      if (db == 0 && s < 3) pn = mkp(s + 1);
+      if (db == NDB - 1) {
+        const bf16x2_t x0 = {pc[0], pc[1]}, x1 = {pc[2], pc[3]};
+        const bf16x2_t x2 = {pc[4], pc[5]}, x3 = {pc[6], pc[7]};
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(x0, one, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(x1, one, ps1, false);
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(x2, one, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, ps1, false);
+        pc = pn;
       }
+    }
+    l_part += ps0 + ps1;
+    // Order: step-0 exponentials and the first V reads; then per MFMA the read RA ahead, the
+    // MFMA, and a slice of the next step's VALU work.
+    __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RA, 0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (m + RA < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
     }
   };
 
@@ -387,9 +402,7 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
     mask_tile(j, cur);
     if (keep_prev) {
       rescale_to(m_prev);
-      bf16x8_t pf[4];
-      exp_p(prev, pf);
-      pv(pf, (j - 1) & 1);
+      exp_pv(prev, (j - 1) & 1);
     }
     publish_margin(j, vote_tile(j, cur));
   };
@@ -398,9 +411,7 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
     __syncthreads();
     if (decision(n_tiles - 1, read_votes(n_tiles - 1))) {
       rescale_to(m_run);
-      bf16x8_t pf[4];
-      exp_p(last, pf);
-      pv(pf, (n_tiles - 1) & 1);
+      exp_pv(last, (n_tiles - 1) & 1);
     }
   };
   f32x16_t sa[2], sb[2];
