@@ -13,7 +13,7 @@
 // fp32 plus the score tile would not fit the 256 accumulation registers of a wave. Per key tile
 // of 64 keys:
 //   * the K tile (64 x 576 bf16, 72 KB) goes from HBM straight into LDS (global_load_lds_dwordx4,
-//     two stages); the next tile streams in while this one is used;
+//     two stages); the next tile's loads are issued between the MFMAs of this tile's scores;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 over 36 k-steps: A = K from LDS, B = the wave's
 //     32 query rows kept in registers (144 VGPRs);
 //   * tile row max, skip vote (ballot, LDS, barrier) exactly as in prefill;
@@ -25,6 +25,7 @@
 // tile's bytes in order (64 chunks per wave-wide load), so each load is 1 KB of contiguous K.
 // Splits write normalised partial O and base-2 LSE to the workspace; the split merge combines.
 #include "internal.h"
+#include "lds_dma.h"
 
 #include <math.h>
 
@@ -34,7 +35,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr float kLn2 = 0.6931471805599453f;
@@ -106,18 +106,17 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 
   // Tile loads: wave-wide load i fills tile bytes [1024 i, 1024 i + 1024); lane L fills chunk
   // t = 64 i + L of the tile, i.e. row t / 72 at physical chunk t % 72, which holds logical
-  // chunk swz(row, t % 72).
-  auto issue = [&](int tile, int st) {
-    const int k0 = tile * kBlockC;
-    for (int i = wv; i < kLoadsPerTile; i += NW) {
-      const int t = 64 * i + lane;
-      const int r = t / kChunks;
-      const int pc = t - r * kChunks;
-      const int key = min(k0 + r, seq_len - 1);  // rows past the end load a real row (masked)
-      const __bf16 *gp = Kg + (int64_t)key * p.k_ss + 8 * swz(r, pc);
-      __builtin_amdgcn_global_load_lds((const void *)gp, (lds_void_t *)(&smem[st][i * 1024]), 16,
-                                       0, 0);
-    }
+  // chunk swz(row, t % 72). This wave's load nn (0 .. 17) is wave-wide load i = wv + 4 nn.
+  auto issue_one = [&](int tile, int st, int nn) {
+    int ln = lane;  // opaque: recomputed per load instead of kept live across the MFMAs
+    asm volatile("" : "+v"(ln));
+    const int i = wv + NW * nn;
+    const int t = 64 * i + ln;
+    const int r = t / kChunks;
+    const int pc = t - r * kChunks;
+    const int key = min(tile * kBlockC + r, seq_len - 1);  // rows past the end load a real row
+    const __bf16 *gp = Kg + (int64_t)key * p.k_ss + 8 * swz(r, pc);
+    lds_dma16(gp, lds_addr(&smem[st][i * 1024]));
   };
 
   // V^T transpose-read offsets (see prefill_mfma.hip for the lane mapping): as a source lane,
@@ -130,9 +129,11 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   float m_run = -INFINITY, m_ref = -INFINITY, l_part = 0.f;
   unsigned visited = 0, skipped = 0;
 
-  // S^T = K Q^T. K fragments are read KPF k-steps ahead of their MFMAs; the scheduling hints
-  // keep that bounded look-ahead (left alone, the scheduler hoists all 72 reads).
-  auto compute_s = [&](int st, f32x16_t *sacc) {
+  // S^T = K Q^T. K fragments are read KPF k-steps ahead of their MFMAs. The next tile's loads (next_tile >= 0) go out one per two k-steps between the MFMAs: each
+  // inline-asm load is a scheduling boundary, so the reads and MFMAs between two loads stay in
+  // source order, and a wave (alone on its SIMD) never stalls on a full load queue with its matrix
+  // core idle.
+  auto compute_s = [&](int st, f32x16_t *sacc, int next_tile) {
     constexpr int KPF = 2;
     sacc[0] = (f32x16_t)0.f;
     sacc[1] = (f32x16_t)0.f;
@@ -158,12 +159,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s][kb], qf[s], sacc[kb], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KPF, 0);
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (s + KPF < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if ((s & 1) && next_tile >= 0) issue_one(next_tile, st ^ 1, s >> 1);
     }
   };
 
@@ -264,13 +260,14 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 
   // Two barriers per tile: the first publishes tile j (and frees the other stage for tile
   // j + 1, which then streams in during this tile's work), the second publishes the votes.
-  if (n_tiles > 0) issue(t_begin, 0);
+  if (n_tiles > 0) {
+    for (int nn = 0; nn < kLoadsPerTile / NW; ++nn) issue_one(t_begin, 0, nn);
+  }
   for (int j = 0; j < n_tiles; ++j) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < n_tiles) issue(t_begin + j + 1, (j + 1) & 1);
     f32x16_t sacc[2];
-    compute_s(j & 1, sacc);
+    compute_s(j & 1, sacc, j + 1 < n_tiles ? t_begin + j + 1 : -1);
     mask_tile(t_begin + j, sacc);
     vote_tile(j, sacc);
     __syncthreads();

@@ -27,6 +27,7 @@
 // and blocks are dealt to the 8 XCDs so each XCD works through contiguous runs of units: the
 // query heads that share K/V read it through the same L2 at about the same time.
 #include "internal.h"
+#include "lds_dma.h"
 
 #include <math.h>
 
@@ -37,7 +38,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr float kLn2 = 0.6931471805599453f;
@@ -80,23 +80,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // since the last rescale: P = 2^(s - m_ref) then stays below 2^8, and the algebra is exact.
 constexpr float kRescaleSlack = 8.f;
 
-
-// HBM -> LDS copies issued as inline assembly. The compiler does not see them as LDS writes, so
-// it adds no conservative "wait for every load" in front of LDS reads of the other pipeline
-// stages; the kernel's own s_waitcnt + barrier at the top of each step orders the data. M0 holds
-// the wave's LDS destination (lane i lands at M0 + size * i); nothing else in this kernel uses M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved to the compiler; see above
-__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
 
 template <int D>
 struct Geo {
