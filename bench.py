@@ -44,6 +44,7 @@ DECODE = dict(B=64, Hq=32, Hkv=8, L=32768, d=128, cluster_len=512, seed=3000)
 DECODE_BETA = 16.0
 MLA = dict(B=32, Hq=128, L=65536, cluster_len=1024, seed=5000)
 MLA_BETA = 16.0
+CALIB_BETA = 16.0  # smoother score spread than the headline's, so the swept curve has a slope
 
 
 def _parse():
@@ -53,7 +54,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="same as --part prefill")
-    ap.add_argument("--part", choices=("all", "prefill", "decode", "mla"), default="all",
+    ap.add_argument("--part", choices=("all", "prefill", "decode", "mla", "calib"), default="all",
                     help="prefill: the headline call only; decode / mla: that decode only "
                          "(profiling runs isolate one kernel this way)")
     ap.add_argument("--a", type=float, default=None,
@@ -368,6 +369,43 @@ def _mla_part(F, torch, args, dev, stream, out):
                          "points": mla}
 
 
+def _calib_part(F, torch, args, dev, stream, out):
+    """Calibration sweep (talk notes, Algorithm 2): one lambda = 0 call per length records the
+    tile margins; the skip fraction at every candidate follows from them. Reports the fixed-
+    threshold sparsity per length (the setting of the notes' Table 6), the fitted
+    lambda * L = a exp(b S) and the sparsity the fitted model gives at each length."""
+    from flashattention_softmax_threshold_amd import calibration as C
+    from flashattention_softmax_threshold_amd.inputs import prefill_inputs
+
+    P = PREFILL
+    factors = [2.0 ** e for e in range(-2, 13)]
+    rows, points, curves = [], [], {}
+    for L in (2048, 4096, 8192, 16384):
+        q, k, v = prefill_inputs(B=P["B"], L=L, Hq=P["Hq"], Hkv=P["Hkv"], d=P["d"],
+                                 cluster_len=P["cluster_len"], dtype=torch.bfloat16, device=dev,
+                                 seed=P["seed"] + L, beta=CALIB_BETA, sinks=P["sinks"])
+        ms = _time_calls(lambda: C.prefill_margins(q, k, v, causal=True, stream=stream),
+                         max(args.steps // 10, 3), max(args.warmup // 10, 1), stream)
+        margin, status = C.prefill_margins(q, k, v, causal=True, stream=stream)
+        torch.cuda.synchronize()
+        margin, status = margin.cpu(), status.cpu()
+        fixed, vis = F.blasst_sparsity_curve(margin, status, [1e-3])
+        points += C.observations(margin, status, L, factors)
+        curves[L] = (margin, status)
+        rows.append({"L": L, "sweep_call_ms": ms, "visited_tiles": vis,
+                     "sparsity_at_lambda_1e-3": fixed[0]})
+        del q, k, v
+    a, b = C.fit(points)
+    for r in rows:
+        m, st = curves[r["L"]]
+        got, _ = F.blasst_sparsity_curve(m, st, [a * math.exp(b * t) / r["L"] for t in (0.3, 0.5)])
+        r["fitted_model_sparsity_at_targets_0.3_0.5"] = got
+    out["calibration"] = {"workload": "causal GQA prefill B1 Hq32/Hkv8 d128 bf16, 256-token "
+                                      f"clusters, centre gain {CALIB_BETA}, L = 2K..16K",
+                          "fit": {"a": a, "b": b}, "lengths": rows}
+    _progress(f"calibration: a={a:.4g} b={b:.4g}")
+
+
 def main():
     args = _parse()
     if args.counter_summary:
@@ -412,6 +450,8 @@ def main():
         _decode_part(F, torch, args, dev, stream, out)
     if args.part in ("all", "mla"):
         _mla_part(F, torch, args, dev, stream, out)
+    if args.part in ("all", "calib"):
+        _calib_part(F, torch, args, dev, stream, out)
     if headline is not None and not args.no_cpu_baseline:
         q, k, v, lam, br, bc = headline
         _progress("cpu baseline (oracle, about 12 s)")

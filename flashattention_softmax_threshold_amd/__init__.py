@@ -43,6 +43,7 @@ TILE_NOT_VISITED = 2
 
 EXPORTED = (
     "blasst_status_string", "blasst_resolve_lambda", "blasst_timestep_gate",
+    "blasst_sparsity_curve", "blasst_fit_calibration",
     "blasst_prefill_tiles", "blasst_attn_prefill", "blasst_decode_plan",
     "blasst_decode_workspace_size", "blasst_attn_decode",
 )
@@ -128,6 +129,12 @@ def load_library():
         lib.blasst_timestep_gate.argtypes = [ctypes.c_double, I32, ctypes.c_double,
                                              ctypes.POINTER(I32)]
         lib.blasst_timestep_gate.restype = ctypes.c_int
+        D = ctypes.POINTER(ctypes.c_double)
+        lib.blasst_sparsity_curve.argtypes = [P, P, ctypes.c_int64, D, I32, D,
+                                              ctypes.POINTER(ctypes.c_int64)]
+        lib.blasst_sparsity_curve.restype = ctypes.c_int
+        lib.blasst_fit_calibration.argtypes = [D, D, D, I32, D, D]
+        lib.blasst_fit_calibration.restype = ctypes.c_int
         lib.blasst_prefill_tiles.argtypes = [ctypes.POINTER(_PrefillArgs), ctypes.POINTER(I32),
                                              ctypes.POINTER(I32)]
         lib.blasst_prefill_tiles.restype = ctypes.c_int
@@ -174,6 +181,48 @@ def blasst_timestep_gate(disabled_until_timestep: float, t: float | None) -> boo
                                                float("nan") if t is None else float(t),
                                                ctypes.byref(act)), "blasst_timestep_gate")
     return bool(act.value)
+
+
+def blasst_sparsity_curve(tile_margin, tile_status, lambdas):
+    """Skip fraction at each candidate lambda from one call's tile_margin / tile_status outputs
+    (torch tensors or arrays, any device; copied to the host). Returns (sparsity list, visited)."""
+    import numpy as np
+
+    def host(x, dt):
+        if hasattr(x, "detach"):
+            x = x.detach().cpu().numpy()
+        return np.ascontiguousarray(np.asarray(x), dtype=dt).ravel()
+
+    m = host(tile_margin, np.float32)
+    st = host(tile_status, np.uint8)
+    if m.size != st.size:
+        raise ValueError("tile_margin and tile_status differ in size")
+    lam = host(lambdas, np.float64)
+    out = np.zeros(lam.size, dtype=np.float64)
+    vis = ctypes.c_int64(0)
+    dp = ctypes.POINTER(ctypes.c_double)
+    _check(load_library().blasst_sparsity_curve(
+        m.ctypes.data_as(ctypes.c_void_p), st.ctypes.data_as(ctypes.c_void_p), int(m.size),
+        lam.ctypes.data_as(dp), int(lam.size), out.ctypes.data_as(dp), ctypes.byref(vis)),
+        "blasst_sparsity_curve")
+    return out.tolist(), int(vis.value)
+
+
+def blasst_fit_calibration(seq_len, lam, sparsity):
+    """(a, b) of lambda * L = a * exp(b * S) fitted to observations (sequences of equal length)."""
+    import numpy as np
+
+    L = np.ascontiguousarray(seq_len, dtype=np.float64).ravel()
+    la = np.ascontiguousarray(lam, dtype=np.float64).ravel()
+    S = np.ascontiguousarray(sparsity, dtype=np.float64).ravel()
+    if not (L.size == la.size == S.size):
+        raise ValueError("observation arrays differ in size")
+    a, b = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    dp = ctypes.POINTER(ctypes.c_double)
+    _check(load_library().blasst_fit_calibration(
+        L.ctypes.data_as(dp), la.ctypes.data_as(dp), S.ctypes.data_as(dp), int(L.size),
+        ctypes.byref(a), ctypes.byref(b)), "blasst_fit_calibration")
+    return a.value, b.value
 
 
 # ------------------------------------------------------------------------------------------

@@ -87,6 +87,62 @@ blasst_status blasst_resolve_lambda(const blasst_lambda_spec *spec, int64_t max_
   return BLASST_ERR_INVALID_ARG;
 }
 
+// BLASST notes, threshold calibration, Algorithm 2 step 1: the skip fraction at many thresholds
+// from the margins of one call. A skipped tile is a visited tile whose margin is below
+// ln(min(lambda, 1)); lambda = 0 (ln 0 = -inf) skips nothing.
+blasst_status blasst_sparsity_curve(const float *tile_margin, const uint8_t *tile_status,
+                                    int64_t n_tiles, const double *lambdas, int32_t n_lambdas,
+                                    double *sparsity, int64_t *visited) {
+  if (n_tiles < 0 || n_lambdas < 0) return BLASST_ERR_INVALID_ARG;
+  if (n_tiles > 0 && (!tile_margin || !tile_status)) return BLASST_ERR_INVALID_ARG;
+  if (n_lambdas > 0 && (!lambdas || !sparsity)) return BLASST_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n_lambdas; ++i)
+    if (!finite_nonneg(lambdas[i])) return BLASST_ERR_INVALID_ARG;
+  int64_t n_vis = 0;
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    if (tile_status[t] > 2) return BLASST_ERR_INVALID_ARG;
+    n_vis += tile_status[t] != 2;
+  }
+  for (int32_t i = 0; i < n_lambdas; ++i) {
+    const double lam = lambdas[i] < 1.0 ? lambdas[i] : 1.0;
+    const double tau = lam > 0.0 ? log(lam) : -INFINITY;
+    int64_t n_skip = 0;
+    for (int64_t t = 0; t < n_tiles; ++t)
+      n_skip += tile_status[t] != 2 && (double)tile_margin[t] < tau;
+    sparsity[i] = n_vis > 0 ? (double)n_skip / (double)n_vis : 0.0;
+  }
+  if (visited) *visited = n_vis;
+  return BLASST_OK;
+}
+
+// BLASST notes, threshold calibration, Algorithm 2 step 3 (model lambda * L = a * exp(b * S)):
+// ordinary least squares of y = ln(lambda * L) on S.
+blasst_status blasst_fit_calibration(const double *seq_len, const double *lambda,
+                                     const double *sparsity, int32_t n, double *a, double *b) {
+  if (!seq_len || !lambda || !sparsity || !a || !b || n < 2) return BLASST_ERR_INVALID_ARG;
+  double ms = 0.0, my = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!(seq_len[i] > 0.0) || !isfinite(seq_len[i]) || !(lambda[i] > 0.0) ||
+        !isfinite(lambda[i]) || !isfinite(sparsity[i]))
+      return BLASST_ERR_INVALID_ARG;
+    ms += sparsity[i];
+    my += log(lambda[i] * seq_len[i]);
+  }
+  ms /= n;
+  my /= n;
+  double sxx = 0.0, sxy = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    const double dx = sparsity[i] - ms;
+    sxx += dx * dx;
+    sxy += dx * (log(lambda[i] * seq_len[i]) - my);
+  }
+  if (!(sxx > 0.0)) return BLASST_ERR_INVALID_ARG;
+  *b = sxy / sxx;
+  *a = exp(my - *b * ms);
+  if (!isfinite(*a) || !isfinite(*b)) return BLASST_ERR_INVALID_ARG;
+  return BLASST_OK;
+}
+
 // "Skip-Softmax" page, "Timestep gating": dense while t is above the cutoff; cutoff 0 is the
 // "gate off" sentinel; without a published t a positive cutoff keeps the call dense.
 blasst_status blasst_timestep_gate(double disabled_until_timestep, int32_t has_t, double t,

@@ -97,6 +97,34 @@ blasst_status blasst_resolve_lambda(const blasst_lambda_spec *spec, int64_t max_
                                     double *lambda_out);
 
 /* ------------------------------------------------------------------------------------------
+ * Calibration (BLASST notes, threshold calibration, Algorithm 2 steps 1-3 and Eq. 3).
+ *
+ * blasst_sparsity_curve: step 1, many candidate thresholds from one pass. A tile's margin
+ * (tile_max - running_max, natural log, as the attention calls write to tile_margin) does not
+ * depend on lambda -- the running max advances whether or not a tile is skipped -- so the tiles a
+ * call with threshold lambda skips are exactly the visited tiles with margin < ln(min(lambda, 1)).
+ *   tile_margin, tile_status: host arrays of n_tiles entries as one attention call wrote them
+ *     (status 0 or 1 = visited, 2 = not visited; any other status is an error).
+ *   lambdas: n_lambdas finite non-negative candidates.
+ *   sparsity (out, n_lambdas): skipped / visited for each candidate (0 when nothing was visited).
+ *   visited (out, may be NULL): the number of visited tiles.
+ * Errors: NULL arrays with a positive count, n_tiles or n_lambdas < 0, a bad lambda, an unknown
+ * status -> BLASST_ERR_INVALID_ARG. Host memory only; no device call.
+ *
+ * blasst_fit_calibration: step 3, the exponential model lambda * L = a * exp(b * S) fitted by
+ * least squares on ln(lambda * L) = ln a + b S over n observations (seq_len L > 0, lambda > 0,
+ * sparsity S finite). The (a, b) it returns feed BLASST_TARGET_SPARSITY.
+ * Errors: NULL pointers, n < 2, a non-positive or non-finite L or lambda, non-finite S, or all S
+ * equal -> BLASST_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------------------------ */
+blasst_status blasst_sparsity_curve(const float *tile_margin, const uint8_t *tile_status,
+                                    int64_t n_tiles, const double *lambdas, int32_t n_lambdas,
+                                    double *sparsity, int64_t *visited);
+
+blasst_status blasst_fit_calibration(const double *seq_len, const double *lambda,
+                                     const double *sparsity, int32_t n, double *a, double *b);
+
+/* ------------------------------------------------------------------------------------------
  * Timestep gate ("Skip-Softmax" page, "Timestep gating"): whether skipping is active on a
  * diffusion step with normalised timestep t in [0, 1] (decreasing over the run).
  *   disabled_until_timestep == 0: the gate is off, skipping is active on every step (t unused).

@@ -402,3 +402,37 @@ def decode(q, k, v, *, kv_len=None, block_r: int, block_c: int, num_splits: int 
 def default_scale(d_qk: int) -> float:
     """1/sqrt(d_qk), the scaling of the attention definition in "The Hitchhiker's Guide"."""
     return 1.0 / math.sqrt(d_qk)
+
+
+# ------------------------------------------------------------------------------------------
+# Calibration ("BLASST: Dynamic BLocked Attention Sparsity via Softmax Thresholding" talk notes,
+# threshold calibration, Algorithm 2 steps 1-3 and Eq. 3). Plain numpy restatements.
+# ------------------------------------------------------------------------------------------
+
+def sparsity_curve(tile_margin, tile_status, lambdas):
+    """Skip fraction at each lambda from one run's per-tile margins (natural log).
+
+    A visited tile (status 0 or 1) is skipped at threshold lambda exactly when its margin is below
+    ln(min(lambda, 1)); lambda = 0 skips nothing. Returns (list of fractions, visited count)."""
+    m = np.asarray(tile_margin, dtype=np.float64).ravel()
+    st = np.asarray(tile_status).ravel()
+    vis = st != 2
+    n_vis = int(vis.sum())
+    out = []
+    for lam in np.asarray(lambdas, dtype=np.float64).ravel():
+        lam = min(float(lam), 1.0)
+        tau = math.log(lam) if lam > 0.0 else -math.inf
+        n_skip = int(np.sum(vis & (m < tau)))
+        out.append(n_skip / n_vis if n_vis else 0.0)
+    return out, n_vis
+
+
+def fit_calibration(seq_len, lam, sparsity):
+    """(a, b) of the model lambda * L = a * exp(b * S): least squares of ln(lambda L) = ln a + b S."""
+    L = np.asarray(seq_len, dtype=np.float64).ravel()
+    la = np.asarray(lam, dtype=np.float64).ravel()
+    S = np.asarray(sparsity, dtype=np.float64).ravel()
+    y = np.log(la * L)
+    X = np.stack([np.ones_like(S), S], axis=1)
+    (ln_a, b), *_ = np.linalg.lstsq(X, y, rcond=None)
+    return float(math.exp(ln_a)), float(b)

@@ -207,3 +207,51 @@ def test_decode_rejects_bad_arguments_before_launch():
     a.num_splits = 1
     a.heads_kv = 3
     assert lib.blasst_attn_decode(ctypes.byref(a), None, 0, None) == F.BLASST_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------------------------------
+# Calibration entry points (host only) against the oracle's restatement
+# ------------------------------------------------------------------------------------------
+def test_sparsity_curve_matches_oracle():
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(5)
+    n = 5000
+    margins = -np.abs(rng.standard_normal(n) * 4).astype(np.float32)
+    margins[:50] = 0.0                               # tiles that set a new maximum
+    margins[50:60] = np.float32(math.log(0.25))      # exactly at a candidate's ln(lambda)
+    margins[60:70] = -np.inf                         # no row saw a key
+    status = rng.integers(0, 3, n).astype(np.uint8)  # 2 = not visited
+    lams = [0.0, 1e-3, 0.01, 0.25, 0.5, 1.0, 2.0]
+    got, vis = F.blasst_sparsity_curve(margins, status, lams)
+    # The oracle compares in float64 against ln(lambda) exactly like the library does.
+    want, vis_o = oracle.sparsity_curve(margins, status, lams)
+    assert vis == vis_o == int((status != 2).sum())
+    assert got == want
+    assert got[0] == 0.0 and got[-1] == got[-2]      # lambda = 0 skips nothing; lambda > 1 clamps
+
+
+def test_fit_calibration_matches_oracle_and_refuses_bad_input():
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(9)
+    L = rng.choice([4096, 8192, 32768], 40).astype(float)
+    S = rng.uniform(0.2, 0.9, 40)
+    lam = 300 * np.exp(5 * S) / L * np.exp(rng.normal(0, 0.1, 40))
+    a, b = F.blasst_fit_calibration(L, lam, S)
+    ao, bo = oracle.fit_calibration(L, lam, S)
+    assert a == pytest.approx(ao, rel=1e-10) and b == pytest.approx(bo, rel=1e-10)
+    with pytest.raises(F.BlasstError):
+        F.blasst_fit_calibration([1000], [1e-3], [0.5])                   # one point
+    with pytest.raises(F.BlasstError):
+        F.blasst_fit_calibration([1000, 2000], [1e-3, 1e-3], [0.5, 0.5])  # S all equal
+    with pytest.raises(F.BlasstError):
+        F.blasst_fit_calibration([1000, 2000], [0.0, 1e-3], [0.4, 0.5])   # lambda 0
+    with pytest.raises(F.BlasstError):
+        F.blasst_sparsity_curve([0.0], [7], [0.5])                          # unknown status
+    with pytest.raises(F.BlasstError):
+        F.blasst_sparsity_curve([0.0], [0], [-1.0])                         # negative lambda

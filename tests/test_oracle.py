@@ -373,3 +373,56 @@ def test_forced_decisions_mode():
     o_cf = softmax(np.where(cols[None, :], s, -np.inf), axis=1) @ v
     np.testing.assert_allclose(r["o"], o_cf, rtol=1e-10, atol=1e-11)
     assert r["skipped"] == int(pattern.sum())
+
+
+# ------------------------------------------------------------------------------------------
+# Calibration (BLASST talk notes, threshold calibration: Algorithm 2, Eq. 3)
+# ------------------------------------------------------------------------------------------
+def test_fit_calibration_hand_example():
+    # ln(lambda L) = 1, 2, 4 at S = 0, 0.5, 1. By hand: mean S = 1/2, mean y = 7/3,
+    # Sxy = (-1/2)(-4/3) + (1/2)(5/3) = 3/2, Sxx = 1/2, so b = 3 and ln a = 7/3 - 3/2 = 5/6.
+    a, b = oracle.fit_calibration([1, 1, 1], [math.e, math.e ** 2, math.e ** 4], [0, 0.5, 1])
+    assert b == pytest.approx(3.0, abs=1e-12)
+    assert a == pytest.approx(math.exp(5 / 6), rel=1e-12)
+
+
+def test_fit_calibration_recovers_the_wan_coefficients_from_model_points():
+    # Points generated by the page's model lambda * L = a * exp(b * S) with the Wan 2.2
+    # coefficients ("Skip-Softmax calibration config") at several lengths and sparsities.
+    g = json.load(open(os.path.join(GOLDEN, "wan22_calibration.json")))
+    a0, b0 = g["a"], g["b"]
+    L, lam, S = [], [], []
+    for n in (4096, 16384, 75600):
+        for s in (0.3, 0.5, 0.7, 0.9):
+            L.append(n)
+            S.append(s)
+            lam.append(a0 * math.exp(b0 * s) / n)
+    a, b = oracle.fit_calibration(L, lam, S)
+    assert a == pytest.approx(a0, rel=1e-9)
+    assert b == pytest.approx(b0, rel=1e-9)
+
+
+def test_sparsity_curve_from_one_pass_equals_separate_runs():
+    # Algorithm 2 step 1 sweeps many thresholds in one pass. The margins of a lambda = 0 run must
+    # give, for every candidate, exactly the skip fraction of a run made with that candidate.
+    torch.manual_seed(3)
+    L, Hq, Hkv, d = 320, 2, 1, 16
+    idx = torch.arange(L) // 32
+    cen = torch.randn(L // 32 + 1, d, dtype=torch.float64) * 8 / math.sqrt(d)
+    k = (3 * cen[idx] + 0.5 * torch.randn(L, d, dtype=torch.float64))[None, :, None, :]
+    q = (cen[idx] + 0.5 * torch.randn(Hq, L, d, dtype=torch.float64)).permute(1, 0, 2)[None]
+    v = torch.randn(1, L, Hkv, d, dtype=torch.float64)
+    kw = dict(causal=True, block_r=32, block_c=32, scale=1 / math.sqrt(d))
+    base = oracle.prefill(q, k, v, lam=0.0, **kw)
+    margins = np.concatenate([u.tile_margin for u in base.units.values()])
+    status = np.concatenate([u.tile_status for u in base.units.values()])
+    lams = [0.0, 1e-4, 1e-3, 1e-2, 0.05, 0.2, 0.6, 1.0, 3.0]
+    curve, n_vis = oracle.sparsity_curve(margins, status, lams)
+    assert n_vis == sum(int(u.visited) for u in base.units.values())
+    for lam, frac in zip(lams, curve):
+        r = oracle.prefill(q, k, v, lam=lam, **kw)
+        vis = sum(int(u.visited) for u in r.units.values())
+        sk = sum(int(u.skipped) for u in r.units.values())
+        assert vis == n_vis
+        assert frac == sk / vis, (lam, frac, sk / vis)
+    assert curve == sorted(curve) and 0 < curve[-2] < 1
