@@ -44,6 +44,7 @@ DECODE = dict(B=64, Hq=32, Hkv=8, L=32768, d=128, cluster_len=512, seed=3000)
 DECODE_BETA = 16.0
 MLA = dict(B=32, Hq=128, L=65536, cluster_len=1024, seed=5000)
 MLA_BETA = 16.0
+PAGE_SIZES = (16, 64)  # paged-cache points of the GQA decode measurement
 CALIB_BETA = 16.0  # smoother score spread than the headline's, so the swept curve has a slope
 
 
@@ -324,9 +325,34 @@ def _decode_part(F, torch, args, dev, stream, out):
                     "hbm_frac": nbytes / (msd * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "speedup_vs_lambda0": (msd0 / msd) if msd0 else None})
         _progress(f"decode gqa a={a:g}: {msd:.4f} ms")
+    # Paged cache: the same keys scattered over shuffled pages of a pool; only the row addresses
+    # change, so the bytes and the decisions are those of the contiguous call.
+    from flashattention_softmax_threshold_amd.inputs import paged_layout
+
+    paged = []
+    la = 16.0 / D["L"]
+    ms_c = next(pt["ms"] for pt in dec if pt["lambda"] == "16/L") if args.a in (None, 16.0) else None
+    for ps in PAGE_SIZES:
+        kp, vp, table = paged_layout(kd, vd, ps, seed=D["seed"] + ps)
+        fn = lambda: F.blasst_attn_decode(qd, kp, vp, kv_len=kvl, lam=la, o=od,  # noqa: E731
+                                          workspace=wsd, block_table=table, max_kv_len=D["L"],
+                                          stream=stream)
+        msp = _time_calls(fn, args.steps, args.warmup, stream)
+        cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+        F.blasst_attn_decode(qd, kp, vp, kv_len=kvl, lam=la, o=od, counters=cnt, workspace=wsd,
+                             block_table=table, max_kv_len=D["L"])
+        torch.cuda.synchronize()
+        vis, sk = (int(x) for x in cnt.cpu().tolist())
+        nbytes = tile_bytes * (2 * vis - sk) + qd.numel() * 2 + od.numel() * 2
+        paged.append({"page_size": ps, "lambda": "16/L", "ms": msp,
+                      "GB/s": nbytes / (msp * 1e-3) / 1e9,
+                      "hbm_frac": nbytes / (msp * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "time_vs_contiguous": (msp / ms_c) if ms_c else None})
+        _progress(f"decode gqa paged {ps}: {msp:.4f} ms")
+        del kp, vp, table
     out["decode_gqa"] = {"workload": "GQA decode B64 Hq32/Hkv8 KV32768 d128 bf16, "
                                      f"centre gain {DECODE_BETA}, tile {brd}x{bcd}, {sd} splits",
-                         "points": dec}
+                         "points": dec, "paged": paged}
 
 
 def _mla_part(F, torch, args, dev, stream, out):

@@ -101,6 +101,8 @@ class _DecodeArgs(ctypes.Structure):
         ("lse", ctypes.c_void_p), ("counters", ctypes.c_void_p),
         ("tile_status", ctypes.c_void_p), ("tile_margin", ctypes.c_void_p),
         ("block_r", ctypes.c_int32), ("block_c", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+        ("pages_per_seq", ctypes.c_int32),
     ]
 
 
@@ -320,9 +322,14 @@ def blasst_attn_prefill(q, k, v, *, causal: bool = False, lam: float = 0.0,
 
 
 def _decode_args(q, k, v, o, *, kv_len, lam, softmax_scale, lse, counters, tile_status,
-                 tile_margin, block_r, block_c, num_splits) -> _DecodeArgs:
+                 tile_margin, block_r, block_c, num_splits, block_table=None,
+                 max_kv_len=None) -> _DecodeArgs:
     B, Hq, Dqk = q.shape
     L, Hkv = k.shape[1], k.shape[2]
+    if block_table is not None:  # k, v are page pools [pages, page_size, Hkv, d]
+        L = block_table.shape[1] * k.shape[1]
+    if max_kv_len is not None:
+        L = int(max_kv_len)
     Dv = v.shape[3]
     a = _DecodeArgs()
     a.dtype = _dtype_code(q)
@@ -342,14 +349,20 @@ def _decode_args(q, k, v, o, *, kv_len, lam, softmax_scale, lse, counters, tile_
     a.tile_status = tile_status.data_ptr() if tile_status is not None else 0
     a.tile_margin = tile_margin.data_ptr() if tile_margin is not None else 0
     a.block_r, a.block_c, a.num_splits = int(block_r), int(block_c), int(num_splits)
+    if block_table is not None:
+        a.block_table = block_table.data_ptr()
+        a.page_size = int(k.shape[1])
+        a.pages_per_seq = int(block_table.shape[1])
     return a
 
 
-def blasst_decode_plan(q, k, v, *, block_r: int = 0, block_c: int = 0, num_splits: int = 0):
+def blasst_decode_plan(q, k, v, *, block_r: int = 0, block_c: int = 0, num_splits: int = 0,
+                       block_table=None, max_kv_len=None):
     """(block_r, block_c, num_splits) a decode call on these tensors uses."""
     a = _decode_args(q, k, v, None, kv_len=None, lam=0.0, softmax_scale=0.0, lse=None,
                      counters=None, tile_status=None, tile_margin=None, block_r=block_r,
-                     block_c=block_c, num_splits=num_splits)
+                     block_c=block_c, num_splits=num_splits, block_table=block_table,
+                     max_kv_len=max_kv_len)
     br, bc, s = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
     _check(load_library().blasst_decode_plan(ctypes.byref(a), ctypes.byref(br), ctypes.byref(bc),
                                              ctypes.byref(s)), "blasst_decode_plan")
@@ -357,19 +370,23 @@ def blasst_decode_plan(q, k, v, *, block_r: int = 0, block_c: int = 0, num_split
 
 
 def blasst_decode_workspace_size(q, k, v, *, block_r: int = 0, block_c: int = 0,
-                                 num_splits: int = 0) -> int:
+                                 num_splits: int = 0, block_table=None, max_kv_len=None) -> int:
     a = _decode_args(q, k, v, None, kv_len=None, lam=0.0, softmax_scale=0.0, lse=None,
                      counters=None, tile_status=None, tile_margin=None, block_r=block_r,
-                     block_c=block_c, num_splits=num_splits)
+                     block_c=block_c, num_splits=num_splits, block_table=block_table,
+                     max_kv_len=max_kv_len)
     return int(load_library().blasst_decode_workspace_size(ctypes.byref(a)))
 
 
 def blasst_attn_decode(q, k, v, *, kv_len=None, lam: float = 0.0, softmax_scale: float = 0.0,
                        o=None, lse=None, counters=None, tile_status=None, tile_margin=None,
                        block_r: int = 0, block_c: int = 0, num_splits: int = 0, workspace=None,
-                       stream=None):
+                       block_table=None, max_kv_len=None, stream=None):
     """BLASST decode: q [B, Hq, Dqk], k [B, L, Hkv, Dqk], v [B, L, Hkv, Dv] (v may be a view of
-    k's first Dv columns: MLA shape); kv_len optional int32 [B] on the device. Returns o."""
+    k's first Dv columns: MLA shape); kv_len optional int32 [B] on the device. Returns o.
+
+    Paged cache: block_table int32 [B, pages_per_seq] on the device, k / v page pools
+    [pages, page_size, Hkv, d]; max_kv_len defaults to pages_per_seq * page_size."""
     import torch
 
     dev = q.device
@@ -380,9 +397,14 @@ def blasst_attn_decode(q, k, v, *, kv_len=None, lam: float = 0.0, softmax_scale:
         o = torch.empty((q.shape[0], q.shape[1], v.shape[3]), dtype=q.dtype, device=dev)
     if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.device != dev):
         raise TypeError("kv_len must be int32 on the same device")
+    if block_table is not None and (block_table.dtype != torch.int32 or block_table.device != dev
+                                    or block_table.dim() != 2 or not block_table.is_contiguous()
+                                    or block_table.shape[0] != q.shape[0]):
+        raise TypeError("block_table must be a contiguous int32 [B, pages_per_seq] on the device")
     a = _decode_args(q, k, v, o, kv_len=kv_len, lam=lam, softmax_scale=softmax_scale, lse=lse,
                      counters=counters, tile_status=tile_status, tile_margin=tile_margin,
-                     block_r=block_r, block_c=block_c, num_splits=num_splits)
+                     block_r=block_r, block_c=block_c, num_splits=num_splits,
+                     block_table=block_table, max_kv_len=max_kv_len)
     lib = load_library()
     need = int(lib.blasst_decode_workspace_size(ctypes.byref(a)))
     if need and workspace is None:

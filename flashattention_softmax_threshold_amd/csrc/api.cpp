@@ -314,6 +314,15 @@ blasst_status blasst_attn_decode(const blasst_decode_args *a, void *workspace,
       !strides_ok(a->v_stride, 3, 8) || !strides_ok(a->o_stride, 2, 8))
     return BLASST_ERR_INVALID_ARG;
   if (a->batch > 65535 || a->heads_kv > 65535) return BLASST_ERR_UNSUPPORTED;
+  int page_shift = 0;
+  if (a->block_table) {
+    // Paged cache: a power-of-two page size and enough pages per sequence for max_kv_len.
+    if (a->page_size < 1 || a->page_size > 4096 || (a->page_size & (a->page_size - 1)) ||
+        a->pages_per_seq < 1 ||
+        (int64_t)a->pages_per_seq * a->page_size < (int64_t)a->max_kv_len)
+      return BLASST_ERR_INVALID_ARG;
+    while ((1 << page_shift) < a->page_size) ++page_shift;
+  }
   const size_t need = blasst_decode_workspace_size(a);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)))
     return BLASST_ERR_WORKSPACE;
@@ -339,6 +348,9 @@ blasst_status blasst_attn_decode(const blasst_decode_args *a, void *workspace,
   p.counters = a->counters;
   p.tile_status = a->tile_status;
   p.tile_margin = a->tile_margin;
+  p.block_table = a->block_table;
+  p.page_shift = page_shift;
+  p.pages_per_seq = a->block_table ? a->pages_per_seq : 0;
   if (s > 1) {
     const size_t rows = (size_t)a->batch * (size_t)a->heads_q * (size_t)s;
     const size_t o_bytes = ((rows * (size_t)a->head_dim_v * sizeof(float) + 255) / 256) * 256;

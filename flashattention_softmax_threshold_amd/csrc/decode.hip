@@ -49,7 +49,7 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 &u, float *f) {
   }
 }
 
-template <int D, int RB>
+template <int D, int RB, bool PAGED>
 __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
   constexpr int STEPS = D / 32;  // k-steps of one 16x16x32 MFMA chain
   constexpr int CPR = D / 8;     // 16-byte chunks per key row
@@ -79,8 +79,36 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
   const int t_split_end = min(t_begin + p.tiles_per_split, p.n_tiles);
   const int t_end = min(t_split_end, seq_tiles);
 
-  const __bf16 *__restrict__ Kg = (const __bf16 *)p.k + b * p.k_sb + g * p.k_sh;
-  const __bf16 *__restrict__ Vg = (const __bf16 *)p.v + b * p.v_sb + g * p.v_sh;
+  // Row of key `key` of this sequence and KV head: contiguous (base + key * row stride) or, for
+  // a paged cache, row key % page_size of page block_table[b][key / page_size] (the batch stride
+  // is then the page stride). Only keys below seq_len are ever addressed.
+  const __bf16 *__restrict__ Kg =
+      (const __bf16 *)p.k + (PAGED ? 0 : b * p.k_sb) + g * p.k_sh;
+  const __bf16 *__restrict__ Vg =
+      (const __bf16 *)p.v + (PAGED ? 0 : b * p.v_sb) + g * p.v_sh;
+  // Paged: each lane holds the page of key `lane` of a tile, loaded one round before the tile is
+  // read (loads complete in issue order, so a table read issued just before the K or V loads
+  // would make them wait for every load in flight); a row's page comes from the lane that holds
+  // it with one cross-lane read.
+  const int32_t *__restrict__ bt = PAGED ? p.block_table + (int64_t)b * p.pages_per_seq : nullptr;
+  const int pmask = (1 << p.page_shift) - 1;
+  auto page_of_lane_key = [&](int tile) -> int {  // page of key tile * 64 + lane (clamped)
+    if constexpr (PAGED) {
+      const int key = min(tile * kBlockC + lane, seq_len - 1);
+      return bt[key >> p.page_shift];
+    } else {
+      return 0;
+    }
+  };
+  auto row_off = [&](int key, int pages, int64_t sb, int64_t ss) -> int64_t {
+    if constexpr (PAGED) {
+      const int pg = __shfl(pages, key & (kBlockC - 1));
+      return (int64_t)pg * sb + (int64_t)(key & pmask) * ss;
+    } else {
+      return (int64_t)key * ss;
+    }
+  };
+  int pages_cur = 0, pages_next = 0;  // paged: this round's tile, the next round's tile
   const int64_t unit_tiles =
       (((int64_t)b * p.Hkv + g) * p.n_rblocks + rb) * (int64_t)p.n_tiles;
 
@@ -95,14 +123,15 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
   }
 
   bf16x8_t kreg[4 * STEPS];
-  auto load_k = [&](int t) {
+  auto load_k = [&](int t, int pages) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int key = t * kBlockC + 16 * kb + n;
+      const int64_t off = row_off(key, pages, p.k_sb, p.k_ss);
 #pragma unroll
       for (int s = 0; s < STEPS; ++s)
         kreg[kb * STEPS + s] = key < seq_len
-                                   ? *(const bf16x8_t *)(Kg + (int64_t)key * p.k_ss + 32 * s + 8 * kgrp)
+                                   ? *(const bf16x8_t *)(Kg + off + 32 * s + 8 * kgrp)
                                    : (bf16x8_t)(__bf16)0.f;
     }
   };
@@ -119,11 +148,15 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
   const int vc = lane % CPR;   // V column chunk of this lane
   const int vk = lane / CPR;   // V key offset of this lane inside a load instruction
 
-  if (n_rounds > 0 && t_begin + wv < t_end) load_k(t_begin + wv);
+  if (n_rounds > 0 && t_begin + wv < t_end) {
+    pages_cur = page_of_lane_key(t_begin + wv);
+    load_k(t_begin + wv, pages_cur);
+  }
 
   for (int r = 0; r < n_rounds; ++r) {
     const int t = t_begin + 4 * r + wv;
     const bool have = t < t_end;
+    if (PAGED && t + 4 < t_end) pages_next = page_of_lane_key(t + 4);  // first load of the round
     f32x4_t sacc[4];
     float mt = -INFINITY;
     if (have) {
@@ -146,7 +179,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sacc[kb][i]);
-      if (t + 4 < t_end) load_k(t + 4);  // next round's K, in flight during this round
+      if (t + 4 < t_end) load_k(t + 4, pages_next);  // next round's K, in flight meanwhile
     } else {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) sacc[kb] = (f32x4_t)0.f;
@@ -180,8 +213,8 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
 #pragma unroll
       for (int kk = 0; kk < VL; ++kk) {
         const int key = t * kBlockC + kk * KPI + vk;
-        vreg[kk] = key < seq_len ? *(const uint4 *)(Vg + (int64_t)key * p.v_ss + 8 * vc)
-                                 : make_uint4(0u, 0u, 0u, 0u);
+        const int64_t off = row_off(key, pages_cur, p.v_sb, p.v_ss);
+        vreg[kk] = key < seq_len ? *(const uint4 *)(Vg + off + 8 * vc) : make_uint4(0u, 0u, 0u, 0u);
       }
     }
     const float M_use = (M == -INFINITY) ? 0.f : M;
@@ -231,6 +264,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
       wave_lds_sync();
     }
     m_run = M;
+    if constexpr (PAGED) pages_cur = pages_next;
 
     if (have) {
       ++visited;
@@ -325,16 +359,21 @@ __global__ __launch_bounds__(128) void split_combine_kernel(DecodeParams p, int 
     p.lse[(int64_t)b * p.Hq + h] = M > -INFINITY ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
-template <int D>
-hipError_t launch_gqa_d(const DecodeParams &p, hipStream_t stream) {
+template <int D, bool PAGED>
+hipError_t launch_gqa_dp(const DecodeParams &p, hipStream_t stream) {
   const dim3 grid(p.num_splits, p.Hkv * p.n_rblocks, p.B);
   if (p.block_r <= 4)
-    hipLaunchKernelGGL((decode_gqa_kernel<D, 4>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_gqa_kernel<D, 4, PAGED>), grid, dim3(256), 0, stream, p);
   else if (p.block_r <= 8)
-    hipLaunchKernelGGL((decode_gqa_kernel<D, 8>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_gqa_kernel<D, 8, PAGED>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_gqa_kernel<D, 16>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_gqa_kernel<D, 16, PAGED>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_gqa_d(const DecodeParams &p, hipStream_t stream) {
+  return p.block_table ? launch_gqa_dp<D, true>(p, stream) : launch_gqa_dp<D, false>(p, stream);
 }
 
 }  // namespace

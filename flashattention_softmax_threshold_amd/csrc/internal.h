@@ -58,6 +58,11 @@ struct DecodeParams {
   // split partials (num_splits > 1): o_part [B, Hq, S, d_v] fp32, lse_part [B, Hq, S] (log2 units)
   float *o_part;
   float *lse_part;
+  // paged cache (block_table != nullptr): key t of sequence b is row t & (2^page_shift - 1) of
+  // page block_table[b * pages_per_seq + (t >> page_shift)]; k_sb / v_sb are the page strides.
+  const int32_t *block_table;
+  int page_shift;
+  int pages_per_seq;
 };
 
 hipError_t launch_decode_gqa(const DecodeParams &p, int head_dim, hipStream_t stream);

@@ -66,6 +66,7 @@ __device__ __forceinline__ int swz(int r, int c) { return c < 64 ? (c ^ (r & 15)
 constexpr int NW = 4;   // waves per workgroup
 constexpr int kBR = 64; // query heads per unit
 
+template <bool PAGED>
 __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[2][kTileBytes];
   __shared__ int sVote[2][NW];
@@ -92,7 +93,21 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   const int t_split_end = min(t_begin + p.tiles_per_split, p.n_tiles);
   const int t_end = min(t_split_end, seq_tiles);
   const int n_tiles = max(0, t_end - t_begin);
-  const __bf16 *__restrict__ Kg = (const __bf16 *)p.k + b * p.k_sb + g * p.k_sh;
+  // Contiguous cache: this sequence's rows; paged cache: the pool (the batch stride is then the
+  // page stride) and this sequence's block-table row.
+  const __bf16 *__restrict__ Kg = (const __bf16 *)p.k + (PAGED ? 0 : b * p.k_sb) + g * p.k_sh;
+  const int32_t *__restrict__ bt = PAGED ? p.block_table + (int64_t)b * p.pages_per_seq : nullptr;
+  // Paged: each lane holds the page of key `lane` of a tile (clamped to the sequence), loaded two
+  // tiles ahead so the copies never wait on the table read; a row's page comes from the lane that
+  // holds it through one cross-lane read.
+  auto page_of_lane_key = [&](int tile) -> int {
+    if constexpr (PAGED) {
+      const int key = min(tile * kBlockC + lane, seq_len - 1);
+      return bt[key >> p.page_shift];
+    } else {
+      return 0;
+    }
+  };
   const int64_t unit_tiles = ((int64_t)b * p.Hkv + g) * p.n_rblocks + rb;
 
   // Q fragments (B operand of S^T = K Q^T): query head my_h, columns 16 s + 8 hh .. + 7.
@@ -107,7 +122,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   // Tile loads: wave-wide load i fills tile bytes [1024 i, 1024 i + 1024); lane L fills chunk
   // t = 64 i + L of the tile, i.e. row t / 72 at physical chunk t % 72, which holds logical
   // chunk swz(row, t % 72). This wave's load nn (0 .. 17) is wave-wide load i = wv + 4 nn.
-  auto issue_one = [&](int tile, int st, int nn) {
+  auto issue_one = [&](int tile, int st, int nn, int pages) {
     int ln = lane;  // opaque: recomputed per load instead of kept live across the MFMAs
     asm volatile("" : "+v"(ln));
     const int i = wv + NW * nn;
@@ -115,7 +130,14 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     const int r = t / kChunks;
     const int pc = t - r * kChunks;
     const int key = min(tile * kBlockC + r, seq_len - 1);  // rows past the end load a real row
-    const __bf16 *gp = Kg + (int64_t)key * p.k_ss + 8 * swz(r, pc);
+    int64_t roff;
+    if constexpr (PAGED) {
+      const int pg = __shfl(pages, key - tile * kBlockC);  // all lanes take part
+      roff = (int64_t)pg * p.k_sb + (int64_t)(key & ((1 << p.page_shift) - 1)) * p.k_ss;
+    } else {
+      roff = (int64_t)key * p.k_ss;
+    }
+    const __bf16 *gp = Kg + roff + 8 * swz(r, pc);
     lds_dma16(gp, lds_addr(&smem[st][i * 1024]));
   };
 
@@ -133,7 +155,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   // inline-asm load is a scheduling boundary, so the reads and MFMAs between two loads stay in
   // source order, and a wave (alone on its SIMD) never stalls on a full load queue with its matrix
   // core idle.
-  auto compute_s = [&](int st, f32x16_t *sacc, int next_tile) {
+  auto compute_s = [&](int st, f32x16_t *sacc, int next_tile, int next_pages) {
     constexpr int KPF = 2;
     sacc[0] = (f32x16_t)0.f;
     sacc[1] = (f32x16_t)0.f;
@@ -159,7 +181,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s][kb], qf[s], sacc[kb], 0, 0, 0);
-      if ((s & 1) && next_tile >= 0) issue_one(next_tile, st ^ 1, s >> 1);
+      if ((s & 1) && next_tile >= 0) issue_one(next_tile, st ^ 1, s >> 1, next_pages);
     }
   };
 
@@ -260,14 +282,23 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 
   // Two barriers per tile: the first publishes tile j (and frees the other stage for tile
   // j + 1, which then streams in during this tile's work), the second publishes the votes.
+  // Paged: `ahead` is the table read of the tile after next; it is taken over (as the pages of
+  // the next tile's copies) only after the wait at the top of the following step.
+  int ahead = 0;
   if (n_tiles > 0) {
-    for (int nn = 0; nn < kLoadsPerTile / NW; ++nn) issue_one(t_begin, 0, nn);
+    const int pages0 = page_of_lane_key(t_begin);
+    if constexpr (PAGED) __builtin_amdgcn_s_waitcnt(0);  // table read landed before any copy
+#pragma unroll
+    for (int nn = 0; nn < kLoadsPerTile / NW; ++nn) issue_one(t_begin, 0, nn, pages0);
+    if (n_tiles > 1) ahead = page_of_lane_key(t_begin + 1);
   }
   for (int j = 0; j < n_tiles; ++j) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    const int pages_next = ahead;  // landed: the wait above drained every load
+    if (PAGED && j + 2 < n_tiles) ahead = page_of_lane_key(t_begin + j + 2);
     f32x16_t sacc[2];
-    compute_s(j & 1, sacc, j + 1 < n_tiles ? t_begin + j + 1 : -1);
+    compute_s(j & 1, sacc, j + 1 < n_tiles ? t_begin + j + 1 : -1, pages_next);
     mask_tile(t_begin + j, sacc);
     vote_tile(j, sacc);
     __syncthreads();
@@ -330,7 +361,10 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 hipError_t launch_decode_mla(const DecodeParams &p, hipStream_t stream) {
   if (p.block_r > kBR) return hipErrorInvalidValue;
   const dim3 grid(p.num_splits, p.n_rblocks, p.B);
-  hipLaunchKernelGGL(decode_mla_kernel, grid, dim3(256), 0, stream, p);
+  if (p.block_table)
+    hipLaunchKernelGGL(decode_mla_kernel<true>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(decode_mla_kernel<false>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -121,3 +121,41 @@ def decode_inputs(*, B: int, Hq: int, Hkv: int, L: int, d_qk: int, d_v: int, clu
     else:
         kv = torch.as_tensor(kv_len, dtype=torch.int32, device=device)
     return q, k, v, kv
+
+
+def paged_layout(k, v, page_size: int, *, seed: int = 0, spare_pages: int = 3, kv_len=None):
+    """Scatter a per-sequence cache into shuffled pages of a shared pool (layout only).
+
+    k [B, L, Hkv, d_qk], v [B, L, Hkv, d_v] (v may be a view of k's first d_v columns) ->
+    (k_pool [P, page_size, Hkv, d_qk], v_pool, block_table int32 [B, ceil(L / page_size)]) with
+    k_pool[block_table[b, t // page_size], t % page_size] == k[b, t] for the keys each sequence
+    uses (all L, or kv_len[b]); pages are drawn in a random order, with `spare_pages` pool pages
+    that no sequence uses, so neighbouring keys of a sequence sit in unrelated pages. When v
+    aliases k's first columns, v_pool is the same view of k_pool.
+    """
+    B, L, Hkv, dq = k.shape
+    dv = v.shape[3]
+    pps = -(-L // page_size)
+    n_pages = B * pps + spare_pages
+    g = _gen("cpu", seed)
+    perm = torch.randperm(n_pages, generator=g)
+    table = perm[: B * pps].view(B, pps).to(torch.int32)
+    aliases = v.data_ptr() == k.data_ptr() and v.stride() == k.stride() and dv < dq
+    k_pool = torch.zeros((n_pages, page_size, Hkv, dq), dtype=k.dtype, device=k.device)
+    v_pool = k_pool[..., :dv] if aliases else torch.zeros((n_pages, page_size, Hkv, dv),
+                                                          dtype=v.dtype, device=v.device)
+    if kv_len is None and L % page_size == 0:  # every page full: one scatter per pool
+        src = k.reshape(B * pps, page_size, Hkv, dq)
+        k_pool[table.view(-1).to(k.device)] = src
+        if not aliases:
+            v_pool[table.view(-1).to(v.device)] = v.reshape(B * pps, page_size, Hkv, dv)
+        return k_pool, v_pool, table.to(k.device)
+    lens = [L] * B if kv_len is None else [int(x) for x in torch.as_tensor(kv_len).cpu().tolist()]
+    for b in range(B):
+        for pg in range(-(-lens[b] // page_size)):
+            t0, t1 = pg * page_size, min((pg + 1) * page_size, lens[b])
+            dst = int(table[b, pg])
+            k_pool[dst, : t1 - t0] = k[b, t0:t1]
+            if not aliases:
+                v_pool[dst, : t1 - t0] = v[b, t0:t1]
+    return k_pool, v_pool, table.to(k.device)

@@ -204,6 +204,17 @@ blasst_status blasst_prefill_tiles(const blasst_prefill_args *args, int32_t *blo
  * block_r <= 16; MLA kernel: head_dim_qk 576, head_dim_v 512, heads_kv 1, v == k, block_c 64,
  * block_r 64. tile_status / tile_margin:
  * [batch, heads_kv, ceil(G / block_r), ceil(max_kv_len / block_c)], G = heads_q / heads_kv.
+ *
+ * Paged KV cache ("The Hitchhiker's Guide -- Phase 08", paged attention: a block table maps a
+ * sequence position to a physical block). With block_table != NULL, k and v point at page pools
+ * addressed [page, row, head, dim] by their strides (k_stride[0] is the page stride, k_stride[1]
+ * the row stride); key t of sequence b is row t % page_size of page
+ * block_table[b * pages_per_seq + t / page_size]. page_size: a power of two in [1, 4096];
+ * pages_per_seq * page_size >= max_kv_len. The table is device int32 memory owned by the caller;
+ * its entries for the keys a sequence uses must name pages inside the pools (they are not
+ * checked on the host: an entry out of range reads outside the pool). Results are bit-identical
+ * to a contiguous cache holding the same keys. block_table == NULL: contiguous per sequence
+ * (page_size and pages_per_seq ignored).
  * ------------------------------------------------------------------------------------------ */
 typedef struct blasst_decode_args {
   blasst_dtype dtype;
@@ -219,6 +230,8 @@ typedef struct blasst_decode_args {
   uint8_t *tile_status;
   float *tile_margin;
   int32_t block_r, block_c, num_splits; /* 0 = default / automatic */
+  const int32_t *block_table;           /* optional paged cache: device [batch, pages_per_seq] */
+  int32_t page_size, pages_per_seq;
 } blasst_decode_args;
 
 /* Resolved launch plan of a decode call: tile shape and split count. */

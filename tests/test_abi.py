@@ -207,6 +207,14 @@ def test_decode_rejects_bad_arguments_before_launch():
     a.num_splits = 1
     a.heads_kv = 3
     assert lib.blasst_attn_decode(ctypes.byref(a), None, 0, None) == F.BLASST_ERR_INVALID_ARG
+    a.heads_kv = 2
+    # Paged cache: the page size must be a power of two in [1, 4096] and the pages must cover
+    # max_kv_len (every case below is refused before anything is launched).
+    a.block_table = 1 << 21
+    for page_size, pages in ((48, 8), (0, 8), (8192, 1), (64, 4), (64, 0)):
+        a.page_size, a.pages_per_seq = page_size, pages
+        assert lib.blasst_attn_decode(ctypes.byref(a), None, 0, None) == F.BLASST_ERR_INVALID_ARG, \
+            (page_size, pages)
 
 
 # ------------------------------------------------------------------------------------------

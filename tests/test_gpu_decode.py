@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import flashattention_softmax_threshold_amd as F
-from flashattention_softmax_threshold_amd.inputs import decode_inputs
+from flashattention_softmax_threshold_amd.inputs import decode_inputs, paged_layout
 
 from parity import (MARGIN_BAND, assert_lse_close, assert_outputs_close, compare_tile_status, need_gpu,
                     oracle_scale)
@@ -15,19 +15,22 @@ from parity import (MARGIN_BAND, assert_lse_close, assert_outputs_close, compare
 pytestmark = pytest.mark.gpu
 
 
-def _run_gpu(q, k, v, kv_len, *, lam, num_splits=0, block_r=0):
+def _run_gpu(q, k, v, kv_len, *, lam, num_splits=0, block_r=0, block_table=None,
+             max_kv_len=None):
     B, Hq, Dqk = q.shape
-    br, bc, S = F.blasst_decode_plan(q, k, v, block_r=block_r, num_splits=num_splits)
+    br, bc, S = F.blasst_decode_plan(q, k, v, block_r=block_r, num_splits=num_splits,
+                                     block_table=block_table, max_kv_len=max_kv_len)
     Hkv = k.shape[2]
     n_rb = -(-(Hq // Hkv) // br)
-    nt = -(-k.shape[1] // bc)
+    nt = -(-(k.shape[1] if max_kv_len is None else max_kv_len) // bc)
     ts = torch.full((B, Hkv, n_rb, max(nt, 1)), 255, dtype=torch.uint8, device=q.device)
     tm = torch.zeros((B, Hkv, n_rb, max(nt, 1)), dtype=torch.float32, device=q.device)
     lse = torch.zeros((B, Hq), dtype=torch.float32, device=q.device)
     cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
     o = F.blasst_attn_decode(q, k, v, kv_len=kv_len, lam=lam, lse=lse, counters=cnt,
                              tile_status=ts, tile_margin=tm, block_r=block_r,
-                             num_splits=num_splits)
+                             num_splits=num_splits, block_table=block_table,
+                             max_kv_len=max_kv_len)
     torch.cuda.synchronize()
     return dict(o=o, lse=lse, status=ts.cpu().numpy(), margin=tm.cpu().numpy(),
                 counters=cnt.cpu().tolist(), br=br, bc=bc, splits=S)
@@ -176,3 +179,59 @@ def test_mla_decode_full_size_sampled():
         st = res["status"]
         assert res["counters"][0] == int((st != 2).sum())
         assert res["counters"][1] == int((st == 1).sum())
+
+
+# ------------------------------------------------------------------------------------------
+# Paged KV cache ("The Hitchhiker's Guide -- Phase 08", paged attention: a block table maps a
+# sequence position to a physical block). Paging changes only where a key row is read, so every
+# output must equal the contiguous call on the same keys bit for bit.
+# ------------------------------------------------------------------------------------------
+def _paged_vs_contiguous(B, Hq, Hkv, L, D, Dv, kv_len, page_sizes, lams, splits, beta, share, seed,
+                         cluster_len=100):
+    need_gpu()
+    mla = Dv != D
+    q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=Hkv, L=L, d_qk=D, d_v=Dv, cluster_len=cluster_len,
+                                 dtype=torch.bfloat16, device="cuda", seed=seed, beta=beta,
+                                 share=share, v_aliases_k=mla, kv_len=kv_len)
+    for ps in page_sizes:
+        kp, vp, table = paged_layout(k, v, ps, seed=seed + ps, kv_len=kvl)
+        for S in splits:
+            for lam in lams:
+                what = f"paged decode B{B} H{Hq}/{Hkv} L{L} d{D}/{Dv} page {ps} S={S} lam={lam}"
+                print(what, flush=True)
+                ref = _run_gpu(q, k, v, kvl, lam=lam, num_splits=S)
+                got = _run_gpu(q, kp, vp, kvl, lam=lam, num_splits=S, block_table=table,
+                               max_kv_len=L)
+                assert got["splits"] == ref["splits"]
+                assert torch.equal(got["o"], ref["o"]), what
+                assert np.array_equal(got["lse"].cpu().numpy(), ref["lse"].cpu().numpy()), what
+                assert np.array_equal(got["status"], ref["status"]), what
+                assert np.array_equal(got["margin"], ref["margin"]), what
+                assert got["counters"] == ref["counters"], what
+    return q, kp, vp, table, kvl, k, v
+
+
+def test_paged_gqa_equals_contiguous_bitwise():
+    _paged_vs_contiguous(B=3, Hq=16, Hkv=4, L=1100, D=128, Dv=128, kv_len=[1100, 517, 0],
+                         page_sizes=(1, 16, 64, 256), lams=(0.0, 16 / 1100), splits=(1, 3),
+                         beta=16.0, share=True, seed=8100)
+
+
+def test_paged_gqa_against_oracle():
+    q, kp, vp, table, kvl, k, v = _paged_vs_contiguous(
+        B=2, Hq=8, Hkv=2, L=700, D=128, Dv=128, kv_len=[700, 333], page_sizes=(32,),
+        lams=(16 / 700,), splits=(2,), beta=16.0, share=True, seed=8200)
+    lam = 16 / 700
+    res = _run_gpu(q, kp, vp, kvl, lam=lam, num_splits=2, block_table=table, max_kv_len=700)
+    kc, vc, qc, kvc = k.cpu(), v.cpu(), q.cpu(), kvl.cpu()
+    ref = oracle.decode(qc, kc, vc, kv_len=kvc, block_r=res["br"], block_c=res["bc"],
+                        num_splits=res["splits"], scale=oracle_scale(128), lam=lam, threads=8)
+    band_mism = _check(res, ref, qc, kc, vc, lam, "paged decode vs oracle", kvc)
+    assert res["counters"][0] == ref.visited
+    assert abs(res["counters"][1] - ref.skipped) <= band_mism
+
+
+def test_paged_mla_equals_contiguous_bitwise():
+    _paged_vs_contiguous(B=2, Hq=128, Hkv=1, L=700, D=576, Dv=512, kv_len=[700, 129],
+                         page_sizes=(16, 64), lams=(0.0, 16 / 700), splits=(1, 2), beta=4.0,
+                         share=True, seed=8300, cluster_len=128)
