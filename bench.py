@@ -44,6 +44,8 @@ DECODE = dict(B=64, Hq=32, Hkv=8, L=32768, d=128, cluster_len=512, seed=3000)
 DECODE_BETA = 16.0
 MLA = dict(B=32, Hq=128, L=65536, cluster_len=1024, seed=5000)
 MLA_BETA = 16.0
+DIT_BETA = 4.0  # the Video-DiT generator's centre gain: skip fraction in the pages' range
+WAN_A, WAN_B = 2822.6209952221557, 4.388250623520793  # "Skip-Softmax calibration config"
 PAGE_SIZES = (16, 64)  # paged-cache points of the GQA decode measurement
 CALIB_BETA = 16.0  # smoother score spread than the headline's, so the swept curve has a slope
 
@@ -55,7 +57,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="same as --part prefill")
-    ap.add_argument("--part", choices=("all", "prefill", "decode", "mla", "calib"), default="all",
+    ap.add_argument("--part", choices=("all", "prefill", "decode", "mla", "calib", "dit"),
+                    default="all",
                     help="prefill: the headline call only; decode / mla: that decode only "
                          "(profiling runs isolate one kernel this way)")
     ap.add_argument("--a", type=float, default=None,
@@ -395,6 +398,44 @@ def _mla_part(F, torch, args, dev, stream, out):
                          "points": mla}
 
 
+def _dit_part(F, torch, args, dev, stream, out):
+    """Video-DiT self-attention (non-causal, 40 heads, 21 frames x 3600 tokens, d 128): lambda from
+    a target sparsity through the Wan 2.2 calibration of the Skip-Softmax page."""
+    from flashattention_softmax_threshold_amd.inputs import prefill_inputs
+
+    L, H, d = 75600, 40, 128
+    q, k, v = prefill_inputs(B=1, L=L, Hq=H, Hkv=H, d=d, cluster_len=60, dtype=torch.bfloat16,
+                             device=dev, seed=4000, beta=DIT_BETA, frame_len=3600, patch_len=60)
+    br, bc = F.blasst_prefill_tiles(q, k)
+    o = torch.empty_like(q)
+    tile_flops = 2.0 * br * bc * d
+    dense_flops = 4.0 * H * d * float(L) * L
+    steps, warm = max(args.steps // 10, 3), max(args.warmup // 10, 2)
+    pts = []
+    ms0 = None
+    for s_t in (None, 0.5, 0.7):
+        lam = 0.0 if s_t is None else F.blasst_resolve_lambda(
+            F.BLASST_TARGET_SPARSITY, L, target_sparsity=s_t, a=WAN_A, b=WAN_B)
+        ms = _time_calls(lambda: F.blasst_attn_prefill(q, k, v, causal=False, lam=lam, o=o,  # noqa
+                                                       stream=stream), steps, warm, stream)
+        cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+        F.blasst_attn_prefill(q, k, v, causal=False, lam=lam, counters=cnt)
+        torch.cuda.synchronize()
+        vis, sk = (int(x) for x in cnt.cpu().tolist())
+        if s_t is None:
+            ms0 = ms
+        ex = tile_flops * (2 * vis - sk) / (ms * 1e-3) / 1e12
+        pts.append({"target_sparsity": s_t, "lambda": lam, "ms": ms, "skip_fraction": sk / vis,
+                    "dense_tflops": dense_flops / (ms * 1e-3) / 1e12, "executed_tflops": ex,
+                    "mfma_frac": ex / BF16_PEAK_TFLOPS, "speedup_vs_lambda0": ms0 / ms,
+                    "ceiling_2/(2-f)": 2.0 / (2.0 - sk / vis)})
+        _progress(f"video dit s={s_t}: {ms:.3f} ms")
+    out["prefill_video_dit"] = {"workload": "non-causal MHA B1 H40 L75600 (21 x 3600) d128 bf16, "
+                                            f"tile {br}x{bc}, frame + 60-token patch clusters, "
+                                            f"centre gain {DIT_BETA}", "points": pts}
+    del q, k, v
+
+
 def _calib_part(F, torch, args, dev, stream, out):
     """Calibration sweep (talk notes, Algorithm 2): one lambda = 0 call per length records the
     tile margins; the skip fraction at every candidate follows from them. Reports the fixed-
@@ -476,6 +517,8 @@ def main():
         _decode_part(F, torch, args, dev, stream, out)
     if args.part in ("all", "mla"):
         _mla_part(F, torch, args, dev, stream, out)
+    if args.part in ("all", "dit"):
+        _dit_part(F, torch, args, dev, stream, out)
     if args.part in ("all", "calib"):
         _calib_part(F, torch, args, dev, stream, out)
     if headline is not None and not args.no_cpu_baseline:
