@@ -81,53 +81,58 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr float kRescaleSlack = 8.f;
 
 
-template <int D>
+template <int D, int NH>
 struct Geo {
   static constexpr int ROW_BYTES = D * 2;                  // one key row of K or V
   static constexpr int CPR = D / 8;                        // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;   // rows one wave-wide 16-byte load fills
   static constexpr int TILE_BYTES = kBlockC * ROW_BYTES;
-  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / kNW;
+  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / (kNW * NH);
   static constexpr int SWZ_V_MASK = CPR - 1;
 };
 
 __device__ __forceinline__ int swz_k(int row, int cpr) { return row & (cpr - 1); }
 __device__ __forceinline__ int swz_v(int row, int cpr) { return (4 * (row & 3)) & (cpr - 1); }
 
-template <int D>
-__global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
-  using G = Geo<D>;
+// NH query heads of one KV group per workgroup (4 waves, i.e. one 128-row unit, per head): the
+// K and V tiles in LDS serve all NH heads, so each wave issues 1 / NH of the loads.
+template <int D, int NH>
+__global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillParams p) {
+  using G = Geo<D, NH>;
   constexpr int RB = G::ROW_BYTES, CPR = G::CPR;
   __shared__ __attribute__((aligned(1024))) char smem[2][2][G::TILE_BYTES];  // [stage][K,V]
-  __shared__ int sVote[2][kNW];     // per tile parity: the vote of tile j is read one tile later
-  __shared__ float sMargin[2][kNW];
+  __shared__ __attribute__((aligned(16))) int sVote[2][kNW * NH];  // [tile parity][wave]
+  __shared__ float sMargin[2][kNW * NH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar
+  const int hs = wv / kNW;  // which of the workgroup's heads
+  const int wq = wv % kNW;  // wave within the head's unit
   const int n = lane & 31;
   const int hh = lane >> 5;
 
   // ---- Which unit: XCD-aware numbering (see the header comment).
   const int grp = p.Hq / p.Hkv;
-  const int n_units = p.B * p.Hq * p.n_qblocks;
+  const int gw = grp / NH;  // workgroups per (KV head, query block)
+  const int n_units = p.B * p.Hkv * gw * p.n_qblocks;
   int u = (int)blockIdx.x;
   if ((n_units & 7) == 0) u = (u & 7) * (n_units >> 3) + (u >> 3);
-  const int per_kv = grp * p.n_qblocks;
+  const int per_kv = gw * p.n_qblocks;
   const int bg = u / per_kv;          // b * Hkv + g
   const int t = u - bg * per_kv;
-  const int qb_r = t / grp;
-  const int hl = t - qb_r * grp;
+  const int qb_r = t / gw;
+  const int hl = t - qb_r * gw;
   const int b = bg / p.Hkv;
   const int g = bg - b * p.Hkv;
-  const int hq = g * grp + hl;
+  const int hq = g * grp + hl * NH + hs;
   const int qb = p.causal ? (p.n_qblocks - 1 - qb_r) : qb_r;
 
   const __bf16 *__restrict__ Qg = (const __bf16 *)p.q + b * p.q_sb + hq * p.q_sh;
   const __bf16 *__restrict__ Kg = (const __bf16 *)p.k + b * p.k_sb + g * p.k_sh;
   const __bf16 *__restrict__ Vg = (const __bf16 *)p.v + b * p.v_sb + g * p.v_sh;
   const int blk_row0 = qb * kBR;
-  const int my_row = blk_row0 + wv * 32 + n;
+  const int my_row = blk_row0 + wq * 32 + n;
   const bool row_ok = my_row < p.Lq;
   int n_tiles = p.n_kvtiles;
   if (p.causal) n_tiles = (min(blk_row0 + kBR, p.Lq) - 1) / kBlockC + 1;
@@ -278,17 +283,19 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
     }
   };
 
-  auto read_votes = [&](int j) { return *(const int4 *)&sVote[j & 1][0]; };
+  // The four votes of this head's unit (one 16-byte LDS read) and the unit's decision; the first
+  // lane of the unit's first wave keeps its counts and observation outputs.
+  const bool bookkeeper = wq == 0 && lane == 0;
+  auto read_votes = [&](int j) { return *(const int4 *)&sVote[j & 1][kNW * hs]; };
   auto decision = [&](int j, int4 vt) {
     const int keep = vt.x | vt.y | vt.z | vt.w;
-    if (tid == 0) {
+    if (bookkeeper) {
       ++visited;
       skipped += keep ? 0u : 1u;
       if (p.tile_status) p.tile_status[unit_tiles + j] = keep ? 0 : 1;
       if (p.tile_margin) {
-        const float dm = fmaxf(fmaxf(sMargin[j & 1][0], sMargin[j & 1][1]),
-                               fmaxf(sMargin[j & 1][2], sMargin[j & 1][3]));
-        p.tile_margin[unit_tiles + j] = dm * kLn2;
+        const float *sm = &sMargin[j & 1][kNW * hs];
+        p.tile_margin[unit_tiles + j] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3])) * kLn2;
       }
     }
     return keep;
@@ -438,7 +445,7 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
           l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
-  if (tid == 0) {
+  if (bookkeeper) {
     if (p.counters) {
       atomicAdd(&p.counters[0], (unsigned long long)visited);
       atomicAdd(&p.counters[1], (unsigned long long)skipped);
@@ -454,12 +461,19 @@ __global__ __launch_bounds__(kNT, 2) void prefill_mfma_kernel(PrefillParams p) {
 
 }  // namespace
 
+template <int D, int NH>
+void launch_nh(const PrefillParams &p, hipStream_t stream) {
+  const dim3 grid((unsigned)(p.B * p.Hq / NH * p.n_qblocks));
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, NH>), grid, dim3(kNT * NH), 0, stream, p);
+}
+
+// Two heads per workgroup when the query heads of a KV head pair up (even group), else one.
 hipError_t launch_prefill_mfma(const PrefillParams &p, int head_dim, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.B * p.Hq * p.n_qblocks));
+  const bool pair = (p.Hq / p.Hkv) % 2 == 0;
   if (head_dim == 128)
-    hipLaunchKernelGGL((prefill_mfma_kernel<128>), grid, dim3(kNT), 0, stream, p);
+    pair ? launch_nh<128, 2>(p, stream) : launch_nh<128, 1>(p, stream);
   else if (head_dim == 64)
-    hipLaunchKernelGGL((prefill_mfma_kernel<64>), grid, dim3(kNT), 0, stream, p);
+    pair ? launch_nh<64, 2>(p, stream) : launch_nh<64, 1>(p, stream);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
