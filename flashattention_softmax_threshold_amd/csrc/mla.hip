@@ -7,18 +7,21 @@
 // work pays there even though V costs no extra traffic: the V tile is the K tile already on chip.
 //
 // Work unit (one workgroup of 4 waves): (sequence b, block of B_r = 64 heads, split of the key
-// range). Wave w owns query heads 32 (w % 2) .. + 31 of the block and output columns
-// 256 (w / 2) .. + 255: both waves of a head pair form the same scores (the Q K^T work is done
-// twice) so that each needs only half of O in accumulation registers -- 32 rows x 512 columns of
-// fp32 plus the score tile would not fit the 256 accumulation registers of a wave. Per key tile
-// of 64 keys:
+// range). Wave w = (row group rg = w % 2, half kh = w / 2) owns query heads 32 rg .. + 31 of the
+// block, the scores of keys 32 kh .. + 31 of each tile, and output columns 256 kh .. + 255: the
+// two waves of a row group form each score once between them (one key half each) and exchange
+// their bf16 P through LDS, so each keeps only half of O (32 rows x 256 columns of fp32) in its
+// accumulation registers. Per key tile of 64 keys:
 //   * the K tile (64 x 576 bf16, 72 KB) goes from HBM straight into LDS (global_load_lds_dwordx4,
 //     two stages); the next tile's loads are issued between the MFMAs of this tile's scores;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 over 36 k-steps: A = K from LDS, B = the wave's
-//     32 query rows kept in registers (144 VGPRs);
-//   * tile row max, skip vote (ballot, LDS, barrier) exactly as in prefill;
-//   * kept tiles: P = exp2(S - m) and the wave's half of O^T (256 x 32) += V^T P^T, V^T read from
-//     the same LDS tile with ds_read_b64_tr_b16.
+//   * S^T (32 keys x 32 heads) = K Q^T with v_mfma_f32_32x32x16_bf16 over 36 k-steps: A = K rows
+//     of the wave's key half from LDS, B = the wave's 32 query rows kept in registers (144 VGPRs);
+//   * the waves publish their partial row maxima through LDS; after one barrier every wave forms
+//     the tile maxima and running maxima of all 64 rows of the unit and takes the test itself,
+//     so all four reach the same decision without exchanging votes;
+//   * kept tiles: P = exp2(S - m_ref) of the wave's key half goes to LDS; after a barrier each
+//     wave holds P for all 64 keys and accumulates O^T (256 x 32) += V^T P^T, V^T read from the
+//     same LDS tile with ds_read_b64_tr_b16.
 // LDS layout: a 576-wide row is 1152 bytes, so every row starts on bank 0 or 32; the 16-byte
 // chunks of a row are XOR-swizzled within groups of 16 (the last 8 chunks within a group of 8)
 // by the row index, which makes the 64-lane K reads conflict-free. The loads are laid out as the
@@ -60,6 +63,12 @@ __device__ __forceinline__ float sum_halves(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+// O and l are rescaled only when some row's max has grown by more than this (base-2 units)
+// since the last rescale: P = 2^(s - m_ref) stays below 2^8; the algebra is exact.
+constexpr float kRescaleSlack = 8.f;
+
 // Physical chunk position of logical chunk c in row r (an involution within its group).
 __device__ __forceinline__ int swz(int r, int c) { return c < 64 ? (c ^ (r & 15)) : (c ^ (r & 7)); }
 
@@ -69,8 +78,11 @@ constexpr int kBR = 64; // query heads per unit
 template <bool PAGED>
 __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[2][kTileBytes];
-  __shared__ int sVote[2][NW];
-  __shared__ float sMargin[2][NW];
+  // Exchange buffers, single: a step's values are read before the next step's first barrier and
+  // rewritten only after it.
+  __shared__ float sPmax[NW][32];                                  // partial row maxima
+  __shared__ __attribute__((aligned(16))) bf16x8_t sP[NW][2][64];  // P of a key half
+  __shared__ float sL[NW][32];                                        // row-sum halves
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -81,11 +93,13 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   const int rb = blockIdx.y;
   const int b = blockIdx.z;
   const int g = 0;  // one latent KV head
-  const int rg = wv & 1;   // row group of this wave
-  const int half = wv >> 1; // output column half of this wave
+  const int rg = wv & 1;  // row group: heads 32 rg .. of the unit
+  const int kh = wv >> 1;  // key half of the scores and column half of O
   const int h0 = rb * kBR;
   const int my_h = h0 + rg * 32 + n;
   const bool row_ok = my_h < p.Hq && (rg * 32 + n) < p.block_r;
+  const bool oth_ok = h0 + (rg ^ 1) * 32 + n < p.Hq && ((rg ^ 1) * 32 + n) < p.block_r;
+  const bool bookkeeper = wv == 0 && lane == 0;  // counts and records the unit's tiles
   int seq_len = p.kv_len ? p.kv_len[b] : p.max_kv_len;
   seq_len = max(0, min(seq_len, p.max_kv_len));
   const int seq_tiles = (seq_len + kBlockC - 1) / kBlockC;
@@ -141,147 +155,114 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     lds_dma16(gp, lds_addr(&smem[st][i * 1024]));
   };
 
-  // V^T transpose-read offsets (see prefill_mfma.hip for the lane mapping): as a source lane,
-  // this lane points at row 16 s + 4 (lane / 32) + (lane % 16) / 4 (+ 8) and columns
-  // 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4) .. + 3 of the tile.
-
   f32x16_t oacc[kDvBlocks];
 #pragma unroll
   for (int db = 0; db < kDvBlocks; ++db) oacc[db] = (f32x16_t)0.f;
-  float m_run = -INFINITY, m_ref = -INFINITY, l_part = 0.f;
+  float m_run = -INFINITY;    // running max of this wave's rows (base 2)
+  float m_run_o = -INFINITY;  // running max of the other row group's rows (for the vote)
+  float m_ref = -INFINITY, l_part = 0.f;
   unsigned visited = 0, skipped = 0;
 
-  // S^T = K Q^T. K fragments are read KPF k-steps ahead of their MFMAs. The next tile's loads (next_tile >= 0) go out one per two k-steps between the MFMAs: each
-  // inline-asm load is a scheduling boundary, so the reads and MFMAs between two loads stay in
-  // source order, and a wave (alone on its SIMD) never stalls on a full load queue with its matrix
-  // core idle.
-  auto compute_s = [&](int st, f32x16_t *sacc, int next_tile, int next_pages) {
+  // S^T for this wave's 32 heads and its 32 keys (key half kh): A = K rows 32 kh + n of stage st,
+  // B = the wave's query fragments; 36 k-steps, K fragments read KPF steps ahead. The next tile's
+  // loads (next_tile >= 0) go out one per two k-steps between the MFMAs: each inline-asm load is
+  // a scheduling boundary, so the reads and MFMAs between two loads stay in source order, and a
+  // wave (alone on its SIMD) never stalls on a full load queue with its matrix core idle.
+  auto compute_s = [&](int st, int next_tile, int next_pages) {
     constexpr int KPF = 2;
-    sacc[0] = (f32x16_t)0.f;
-    sacc[1] = (f32x16_t)0.f;
+    f32x16_t sacc = (f32x16_t)0.f;
     // The per-lane offsets below do not change between tiles; the empty asm makes them opaque
-    // so the compiler recomputes them (a few VALU ops) instead of keeping ~72 of them live.
+    // so the compiler recomputes them (a few VALU ops) instead of keeping them live.
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int nn = ln & 31, hb = ln >> 5;
-    const char *kl = smem[st] + nn * kRowBytes;
-    bf16x8_t fr[kSteps][2];
-    auto rd = [&](int s) {
+    const int r = 32 * kh + nn;  // r & 15 == nn & 15
+    const char *kl = smem[st] + r * kRowBytes;
+    bf16x8_t fr[kSteps];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = 32 * kb + nn;  // r & 15 == nn & 15
-        fr[s][kb] = *(const bf16x8_t *)(kl + kb * 32 * kRowBytes + 16 * swz(r, 2 * s + hb));
-      }
-    };
+    for (int s2 = 0; s2 < KPF; ++s2) fr[s2] = *(const bf16x8_t *)(kl + 16 * swz(r, 2 * s2 + hb));
 #pragma unroll
-    for (int s = 0; s < KPF; ++s) rd(s);
+    for (int s2 = 0; s2 < kSteps; ++s2) {
+      if (s2 + KPF < kSteps)
+        fr[s2 + KPF] = *(const bf16x8_t *)(kl + 16 * swz(r, 2 * (s2 + KPF) + hb));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s2], qf[s2], sacc, 0, 0, 0);
+      if ((s2 & 1) && next_tile >= 0) issue_one(next_tile, st ^ 1, s2 >> 1, next_pages);
+    }
+    return sacc;
+  };
+
+  // Score (key) of accumulator element i: 32 kh + 8 (i / 4) + 4 hh + i % 4 within the tile.
+  auto mask_tile = [&](int tile, f32x16_t &sacc) {
+    const int k0 = tile * kBlockC + 32 * kh;
+    if (k0 + 32 > seq_len) {
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      if (s + KPF < kSteps) rd(s + KPF);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s][kb], qf[s], sacc[kb], 0, 0, 0);
-      if ((s & 1) && next_tile >= 0) issue_one(next_tile, st ^ 1, s >> 1, next_pages);
+      for (int i = 0; i < 16; ++i)
+        if (k0 + 8 * (i >> 2) + 4 * hh + (i & 3) >= seq_len) sacc[i] = -INFINITY;
     }
   };
 
-  auto mask_tile = [&](int tile, f32x16_t *sacc) {
-    const int k0 = tile * kBlockC;
-    if (k0 + kBlockC > seq_len) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (k0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= seq_len) sacc[kb][i] = -INFINITY;
-    }
-  };
-
-  auto vote_tile = [&](int j, const f32x16_t *sacc) {
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
-    mt = max_halves(mt);
-    const float mt2 = __fmul_rn(mt, p.scale_log2);
-    const float delta = (mt2 >= m_run) ? 0.f : __fsub_rn(mt2, m_run);  // exactly 0 at a new max
-    m_run = fmaxf(m_run, mt2);
-    const bool has_key = mt2 > -INFINITY;
-    const bool keep_row = row_ok && has_key && !(delta < p.tau_log2);
-    sVote[j & 1][wv] = __ballot(keep_row) != 0ull;
-    if (p.tile_margin) {
-      float dm = (row_ok && has_key) ? delta : -INFINITY;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) dm = fmaxf(dm, __shfl_xor(dm, o));
-      sMargin[j & 1][wv] = dm;
-    }
-  };
-
-  auto decision = [&](int j) {
-    int keep = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) keep |= sVote[j & 1][w];  // waves of a pair vote alike
-    if (tid == 0) {
-      ++visited;
-      skipped += keep ? 0u : 1u;
-      const int64_t at = unit_tiles * p.n_tiles + t_begin + j;
-      if (p.tile_status) p.tile_status[at] = keep ? 0 : 1;
-      if (p.tile_margin) {
-        float dm = -INFINITY;
-        for (int w = 0; w < NW; ++w) dm = fmaxf(dm, sMargin[j & 1][w]);
-        p.tile_margin[at] = dm * kLn2;
-      }
-    }
-    return keep;
+  // Row test for one row: margin exactly 0 at a new row maximum (mt2 rounded on its own, no
+  // fused multiply-add); returns keep and advances the running max.
+  auto row_test = [&](float tmax, float &mr, bool ok, float &margin) {
+    const float mt2 = __fmul_rn(tmax, p.scale_log2);
+    const float delta = (mt2 >= mr) ? 0.f : __fsub_rn(mt2, mr);
+    mr = fmaxf(mr, mt2);
+    const bool valid = ok && mt2 > -INFINITY;
+    margin = valid ? delta : -INFINITY;
+    return valid && !(delta < p.tau_log2);
   };
 
   auto rescale_to = [&](float m_tile) {
-    if (__ballot(m_tile > m_ref) != 0ull) {
+    if (__ballot(m_tile > m_ref + kRescaleSlack) != 0ull) {
       const float alpha = exp2_fast(m_ref - ((m_tile == -INFINITY) ? 0.f : m_tile));
       l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < kDvBlocks; ++db) oacc[db] *= alpha;
+      m_ref = m_tile;
     }
-    m_ref = m_tile;
   };
 
-  // P = exp2(S - m) and O^T += V^T P^T, one k-step (16 keys) at a time: the 8 exponentials of a
-  // step are formed right before its 16 MFMAs, so only one step's P is live.
-  auto exp_pv = [&](const f32x16_t *sacc, float m_tile, int st) {
-    const float m_use = (m_tile == -INFINITY) ? 0.f : m_tile;
+  // O^T (this wave's 256 columns) += V^T P^T over the tile's 64 keys: k-step s (keys
+  // 16 s .. 16 s + 15) takes the bf16 P operand pf[s] as B and 8 column blocks of V^T
+  // (transpose reads of the row-major tile, stage st) as A, read RA MFMAs ahead.
+  // pf[0..1]: this wave's own P (keys 32 kh .. + 31), pf[2..3]: its partner's (keys
+  // 32 (kh ^ 1) ..); the sum over keys does not depend on their order, so only the V rows read
+  // for a step follow kh (a wave-uniform address term, no operand selection).
+  auto pv = [&](const bf16x8_t *pf, int st) {
+    constexpr int NM = 4 * kDvBlocks;  // 32 MFMAs: (s, db) = (m / 8, m % 8)
+    constexpr int RA = 2;
     int ln = lane;  // opaque, as in compute_s
     asm volatile("" : "+v"(ln));
     const int vrow = 4 * (ln >> 5) + ((ln & 15) >> 2);
     const int vcb = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
     const char *vl = smem[st] + 8 * (ln & 1);
-    float psum = 0.f;
+    auto rdv = [&](int m) {
+      const int s2 = m / kDvBlocks, db = m % kDvBlocks;
+      const int key_step = 2 * (s2 < 2 ? kh : kh ^ 1) + (s2 & 1);  // keys 16 key_step ..
+      const int r0 = 16 * key_step + vrow;
+      const int c = 4 * (kDvBlocks * kh + db) + vcb;  // logical chunk (< 64)
+      const char *p0 = vl + r0 * kRowBytes + 16 * (c ^ (r0 & 15));
+      const char *p1 = vl + (r0 + 8) * kRowBytes + 16 * (c ^ ((r0 + 8) & 15));
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8_t va[RA + 1];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t pf;
+    for (int m = 0; m < RA; ++m) va[m] = rdv(m);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pv = exp2_fast(fmaf(sacc[s >> 1][8 * (s & 1) + e], p.scale_log2, -m_use));
-        psum += pv;
-        pf[e] = (__bf16)pv;
-      }
-      const int r0 = 16 * s + vrow;
-#pragma unroll
-      for (int db = 0; db < kDvBlocks; ++db) {
-        const int c = 4 * (kDvBlocks * half + db) + vcb;  // logical chunk (< 64)
-        const char *p0 = vl + r0 * kRowBytes + 16 * (c ^ (r0 & 15));
-        const char *p1 = vl + (r0 + 8) * kRowBytes + 16 * (c ^ ((r0 + 8) & 15));
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, oacc[db], 0, 0, 0);
-      }
+    for (int m = 0; m < NM; ++m) {
+      if (m + RA < NM) va[(m + RA) % (RA + 1)] = rdv(m + RA);
+      oacc[m % kDvBlocks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m % (RA + 1)],
+                                                                    pf[m / kDvBlocks],
+                                                                    oacc[m % kDvBlocks], 0, 0, 0);
     }
-    l_part += psum;
   };
 
-  // Two barriers per tile: the first publishes tile j (and frees the other stage for tile
-  // j + 1, which then streams in during this tile's work), the second publishes the votes.
+  // Three barriers per kept tile (two per skipped one): (1) tile j is in LDS, the other stage is
+  // free; (2) every wave's partial row maxima are visible -- each wave then takes the test for
+  // all 64 rows of the unit, so the decision needs no vote exchange; (3) kept tiles only: each
+  // wave's bf16 P for its key half is visible to its partner.
   // Paged: `ahead` is the table read of the tile after next; it is taken over (as the pages of
   // the next tile's copies) only after the wait at the top of the following step.
   int ahead = 0;
@@ -292,28 +273,79 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     for (int nn = 0; nn < kLoadsPerTile / NW; ++nn) issue_one(t_begin, 0, nn, pages0);
     if (n_tiles > 1) ahead = page_of_lane_key(t_begin + 1);
   }
+  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
   for (int j = 0; j < n_tiles; ++j) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int pages_next = ahead;  // landed: the wait above drained every load
     if (PAGED && j + 2 < n_tiles) ahead = page_of_lane_key(t_begin + j + 2);
-    f32x16_t sacc[2];
-    compute_s(j & 1, sacc, j + 1 < n_tiles ? t_begin + j + 1 : -1, pages_next);
+    f32x16_t sacc = compute_s(j & 1, j + 1 < n_tiles ? t_begin + j + 1 : -1, pages_next);
     mask_tile(t_begin + j, sacc);
-    vote_tile(j, sacc);
+    {
+      float m[6];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) m[i] = max3f(sacc[3 * i], sacc[3 * i + 1], sacc[3 * i + 2]);
+      m[5] = sacc[15];
+      const float pm = max_halves(max3f(max3f(m[0], m[1], m[2]), max3f(m[3], m[4], m[5]), m[5]));
+      if (hh == 0) sPmax[wv][n] = pm;
+    }
     __syncthreads();
-    if (decision(j)) {
+    float mg_own, mg_oth;
+    const bool keep_own =
+        row_test(fmaxf(sPmax[wv][n], sPmax[wv ^ 2][n]), m_run, row_ok, mg_own);
+    const bool keep_oth = row_test(fmaxf(sPmax[wv ^ 1][n], sPmax[wv ^ 3][n]),
+                                   m_run_o, oth_ok, mg_oth);
+    const bool keep = __ballot(keep_own || keep_oth) != 0ull;
+    if (p.tile_margin) {
+      float dm = fmaxf(mg_own, mg_oth);
+      asm volatile("" : "+v"(dm));  // keeps the reduction inside the branch
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) dm = fmaxf(dm, __shfl_xor(dm, o));
+      if (bookkeeper) p.tile_margin[unit_tiles * p.n_tiles + t_begin + j] = dm * kLn2;
+    }
+    if (bookkeeper) {
+      ++visited;
+      skipped += keep ? 0u : 1u;
+      if (p.tile_status) p.tile_status[unit_tiles * p.n_tiles + t_begin + j] = keep ? 0 : 1;
+    }
+    if (keep) {
       rescale_to(m_run);
-      exp_pv(sacc, m_run, j & 1);
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      bf16x8_t pf[4];  // own P (keys 32 kh + 16 h2 ..), then the partner's
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8_t pk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pk[e] = (__bf16)exp2_fast(fmaf(sacc[8 * h2 + e], p.scale_log2, -m_use));
+        const bf16x2_t x0 = {pk[0], pk[1]}, x1 = {pk[2], pk[3]};
+        const bf16x2_t x2 = {pk[4], pk[5]}, x3 = {pk[6], pk[7]};
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(x0, one, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(x1, one, ps1, false);
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(x2, one, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, ps1, false);
+        pf[h2] = pk;
+        sP[wv][h2][lane] = pk;
+      }
+      l_part += ps0 + ps1;
+      __syncthreads();
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) pf[2 + h2] = sP[wv ^ 2][h2][lane];
+      pv(pf, j & 1);
     }
   }
 
-  // Epilogue: normalised O (or the split's partial) and LSE.
-  const float l_tot = sum_halves(l_part);
+  // Epilogue: the row sum is split over the two key halves of a wave pair (both scaled to the
+  // same m_ref); normalised O (this wave's 256 columns) or the split's partial, and LSE.
+  const float l_mine = sum_halves(l_part);
+  if (hh == 0) sL[wv][n] = l_mine;
+  __syncthreads();
+  const float l_tot = l_mine + sL[wv ^ 2][n];
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (p.num_splits == 1) {
-      __bf16 *orow = (__bf16 *)p.o + b * p.o_sb + (int64_t)my_h * p.o_sh + 256 * half;
+      __bf16 *orow = (__bf16 *)p.o + b * p.o_sb + (int64_t)my_h * p.o_sh + 256 * kh;
 #pragma unroll
       for (int db = 0; db < kDvBlocks; ++db) {
 #pragma unroll
@@ -325,11 +357,11 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
           *(bf16x4_t *)(orow + d0) = ov;
         }
       }
-      if (p.lse && hh == 0 && half == 0)
+      if (p.lse && hh == 0 && kh == 0)
         p.lse[(int64_t)b * p.Hq + my_h] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
       const int64_t row = ((int64_t)b * p.Hq + my_h) * p.num_splits + split;
-      float *op = p.o_part + row * kDv + 256 * half;
+      float *op = p.o_part + row * kDv + 256 * kh;
 #pragma unroll
       for (int db = 0; db < kDvBlocks; ++db) {
 #pragma unroll
@@ -339,10 +371,10 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
                                              oacc[db][4 * ig + 2] * inv, oacc[db][4 * ig + 3] * inv);
         }
       }
-      if (hh == 0 && half == 0) p.lse_part[row] = l_tot > 0.f ? m_ref + __log2f(l_tot) : -INFINITY;
+      if (hh == 0 && kh == 0) p.lse_part[row] = l_tot > 0.f ? m_ref + __log2f(l_tot) : -INFINITY;
     }
   }
-  if (tid == 0) {
+  if (bookkeeper) {
     if (p.counters && visited) {
       atomicAdd(&p.counters[0], (unsigned long long)visited);
       atomicAdd(&p.counters[1], (unsigned long long)skipped);
