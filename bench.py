@@ -243,7 +243,7 @@ def _prefill_part(F, torch, args, dev, stream, out):
     achieved = exec_flops / (ms * 1e-3) / 1e12
     _progress(f"prefill headline: {ms:.4f} ms, skip {skipped / visited:.3f}, "
               f"{achieved:.0f} executed TFLOP/s")
-    traffic = _traffic_from_profile("prefill_mfma.hip", "prefill_mfma_c2_counters.json")
+    traffic = _traffic_from_profile("prefill_mfma.hip", "prefill_mfma_causal_L8192_hbm_counters.json")
     out.update({
         "value": dense_flops / (ms * 1e-3) / 1e12,
         "ms_per_step": ms,
@@ -355,7 +355,9 @@ def _decode_part(F, torch, args, dev, stream, out):
         del kp, vp, table
     out["decode_gqa"] = {"workload": "GQA decode B64 Hq32/Hkv8 KV32768 d128 bf16, "
                                      f"centre gain {DECODE_BETA}, tile {brd}x{bcd}, {sd} splits",
-                         "points": dec, "paged": paged}
+                         "points": dec, "paged": paged,
+                         "traffic_lambda_16/L": _traffic_from_profile(
+                             "decode.hip", "decode_gqa_B64_L32768_hbm_counters.json")}
 
 
 def _mla_part(F, torch, args, dev, stream, out):
@@ -395,7 +397,9 @@ def _mla_part(F, torch, args, dev, stream, out):
         _progress(f"decode mla a={a:g}: {msm:.4f} ms")
     out["decode_mla"] = {"workload": "MLA-shaped decode B32 Hq128 KV65536 d_qk576/d_v512 bf16, "
                                      f"centre gain {MLA_BETA}, tile {brm}x{bcm}, {sm} splits",
-                         "points": mla}
+                         "points": mla,
+                         "traffic_lambda_16/L": _traffic_from_profile(
+                             "mla.hip", "decode_mla_B32_L65536_hbm_counters.json")}
 
 
 def _dit_part(F, torch, args, dev, stream, out):
