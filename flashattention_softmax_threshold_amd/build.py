@@ -23,9 +23,16 @@ FLAGS = [
 ]
 
 
+# Per-file additions. The MLA decode kernel keeps its O accumulator in ordinary VGPRs (MFMA
+# C/D operands in the VGPR form) and its query fragments in AGPRs: with the default choice the
+# compiler copies the 128 accumulator registers out of AGPRs at the top of every key tile.
+FILE_FLAGS = {"mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -22,6 +22,15 @@ __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
                : "v"(g), "s"(lds)
                : "memory", "m0");
 }
+
+// The same copy from a wave-uniform base address (SGPR pair) plus a per-lane 32-bit byte offset:
+// the address arithmetic of a row-per-instruction copy stays on the scalar unit.
+__device__ __forceinline__ void lds_dma16_s(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // The 32-bit LDS address of a __shared__ object, as a wave-uniform value.

@@ -22,10 +22,11 @@
 //   * kept tiles: P = exp2(S - m_ref) of the wave's key half goes to LDS; after a barrier each
 //     wave holds P for all 64 keys and accumulates O^T (256 x 32) += V^T P^T, V^T read from the
 //     same LDS tile with ds_read_b64_tr_b16.
-// LDS layout: a 576-wide row is 1152 bytes, so every row starts on bank 0 or 32; the 16-byte
-// chunks of a row are XOR-swizzled within groups of 16 (the last 8 chunks within a group of 8)
-// by the row index, which makes the 64-lane K reads conflict-free. The loads are laid out as the
-// tile's bytes in order (64 chunks per wave-wide load), so each load is 1 KB of contiguous K.
+// LDS layout: the latent parts of a tile's rows (64 x 1024 bytes) and their rotary parts
+// (64 x 128 bytes) are stored apart, 16-byte chunks XOR-swizzled by the row so that the K and
+// V^T reads are conflict-free. A wave-wide copy then moves either one latent row (1 KB of
+// contiguous K: a wave-uniform row address plus the lane's swizzled chunk offset) or the rotary
+// parts of 8 rows.
 // Splits write normalised partial O and base-2 LSE to the workspace; the split merge combines.
 #include "internal.h"
 #include "lds_dma.h"
@@ -43,11 +44,15 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
-constexpr int kRowBytes = kDqk * 2;                 // 1152
-constexpr int kChunks = kDqk / 8;                   // 72 chunks of 16 bytes per row
+constexpr int kRowBytes = kDqk * 2;                 // 1152 bytes of a K row in HBM
+constexpr int kLatBytes = kDv * 2;                  // 1024: the latent (V) part of a row
+constexpr int kRopeBytes = kRowBytes - kLatBytes;   // 128: the rotary part
+constexpr int kRopeOff = kBlockC * kLatBytes;       // 65536: rotary region of a stage
 constexpr int kTileBytes = kBlockC * kRowBytes;     // 73728
 constexpr int kLoadsPerTile = kTileBytes / 1024;    // 72 wave-wide 16-byte loads
+constexpr int kRowLoads = kBlockC;                  // 64 of them copy one latent row each
 constexpr int kSteps = kDqk / 16;                   // 36 k-steps of S
+constexpr int kLatSteps = kDv / 16;                 // 32 of them over the latent part
 constexpr int kDvBlocks = kDv / 32 / 2;             // 8 output column blocks per wave
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -69,8 +74,13 @@ __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf
 // since the last rescale: P = 2^(s - m_ref) stays below 2^8; the algebra is exact.
 constexpr float kRescaleSlack = 8.f;
 
-// Physical chunk position of logical chunk c in row r (an involution within its group).
-__device__ __forceinline__ int swz(int r, int c) { return c < 64 ? (c ^ (r & 15)) : (c ^ (r & 7)); }
+// LDS stage layout: the latent parts of the 64 rows (1024 bytes each) at 0, the rotary parts
+// (128 bytes each) at kRopeOff. 16-byte chunk c of latent row r sits at chunk c ^ lat_swz(r),
+// chunk c of rotary row r at c ^ (r & 7). lat_swz maps 8 consecutive rows to 8 distinct even (or
+// odd) chunk offsets, so the S reads (8 rows, one chunk) and the transposed V reads (4 rows, two
+// adjacent chunks) each touch distinct banks; the rotary rows alternate bank halves already.
+__device__ __forceinline__ int lat_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
 
 constexpr int NW = 4;   // waves per workgroup
 constexpr int kBR = 64; // query heads per unit
@@ -133,26 +143,40 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
       qf[s] = row_ok ? *(const bf16x8_t *)(qrow + 16 * s + 8 * hh) : (bf16x8_t)(__bf16)0.f;
   }
 
-  // Tile loads: wave-wide load i fills tile bytes [1024 i, 1024 i + 1024); lane L fills chunk
-  // t = 64 i + L of the tile, i.e. row t / 72 at physical chunk t % 72, which holds logical
-  // chunk swz(row, t % 72). This wave's load nn (0 .. 17) is wave-wide load i = wv + 4 nn.
+  // Tile loads: wave load nn < 16 copies latent row i = wv + 4 nn (chunk L ^ lat_swz(i) of the
+  // row from HBM to physical chunk L), loads 16 and 17 the rotary parts of rows 8 jr .. 8 jr + 7,
+  // jr = wv + 4 (nn - 16) (lane L: row 8 jr + L / 8, logical chunk (L % 8) ^ (L / 8) to physical
+  // L % 8). Rows past the end of the sequence copy its last row instead.
   auto issue_one = [&](int tile, int st, int nn, int pages) {
-    int ln = lane;  // opaque: recomputed per load instead of kept live across the MFMAs
-    asm volatile("" : "+v"(ln));
-    const int i = wv + NW * nn;
-    const int t = 64 * i + ln;
-    const int r = t / kChunks;
-    const int pc = t - r * kChunks;
-    const int key = min(tile * kBlockC + r, seq_len - 1);  // rows past the end load a real row
-    int64_t roff;
-    if constexpr (PAGED) {
-      const int pg = __shfl(pages, key - tile * kBlockC);  // all lanes take part
-      roff = (int64_t)pg * p.k_sb + (int64_t)(key & ((1 << p.page_shift) - 1)) * p.k_ss;
+    const uint32_t lds_st = lds_addr(&smem[st][0]);
+    if (nn < kRowLoads / NW) {
+      const int i = wv + NW * nn;
+      const int key = min(tile * kBlockC + i, seq_len - 1);  // wave-uniform
+      const __bf16 *row;
+      if constexpr (PAGED) {
+        const int pg = __builtin_amdgcn_readlane(pages, key - tile * kBlockC);
+        row = Kg + (int64_t)pg * p.k_sb + (int64_t)(key & ((1 << p.page_shift) - 1)) * p.k_ss;
+      } else {
+        row = Kg + (int64_t)key * p.k_ss;
+      }
+      int ln = lane;  // opaque: recomputed per load instead of kept live across the MFMAs
+      asm volatile("" : "+v"(ln));
+      lds_dma16_s(row, (uint32_t)((ln ^ lat_swz(i)) << 4), lds_st + i * kLatBytes);
     } else {
-      roff = (int64_t)key * p.k_ss;
+      const int jr = wv + NW * (nn - kRowLoads / NW);
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int key = min(tile * kBlockC + 8 * jr + (ln >> 3), seq_len - 1);
+      int64_t roff;
+      if constexpr (PAGED) {
+        const int pg = __shfl(pages, key - tile * kBlockC);  // all lanes take part
+        roff = (int64_t)pg * p.k_sb + (int64_t)(key & ((1 << p.page_shift) - 1)) * p.k_ss;
+      } else {
+        roff = (int64_t)key * p.k_ss;
+      }
+      const __bf16 *gp = Kg + roff + kDv + 8 * ((ln & 7) ^ (ln >> 3));
+      lds_dma16(gp, lds_st + kRopeOff + jr * 1024);
     }
-    const __bf16 *gp = Kg + roff + 8 * swz(r, pc);
-    lds_dma16(gp, lds_addr(&smem[st][i * 1024]));
   };
 
   f32x16_t oacc[kDvBlocks];
@@ -176,15 +200,24 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int nn = ln & 31, hb = ln >> 5;
-    const int r = 32 * kh + nn;  // r & 15 == nn & 15
-    const char *kl = smem[st] + r * kRowBytes;
+    const int r = 32 * kh + nn;
+    // k-step s reads logical chunk 2 s + hb of row r: for s < 32 the latent chunk at physical
+    // ((2 s) ^ g) with g = hb ^ lat_swz(r), i.e. byte (lat | 16 g) ^ 32 (s % 8) + 256 (s / 8);
+    // for s >= 32 the rotary chunk (2 (s - 32)) ^ (hb ^ (r & 7)).
+    const uint32_t lat = (uint32_t)(r * kLatBytes) | (uint32_t)((hb ^ lat_swz(r)) << 4);
+    const uint32_t rope = (uint32_t)(kRopeOff + r * kRopeBytes) | (uint32_t)((hb ^ (r & 7)) << 4);
+    const char *sm = smem[st];
+    auto rdk = [&](int s2) {
+      const uint32_t off = s2 < kLatSteps ? ((lat ^ (32u * (s2 & 7))) + 256u * (s2 >> 3))
+                                          : (rope ^ (32u * (s2 - kLatSteps)));
+      return *(const bf16x8_t *)(sm + off);
+    };
     bf16x8_t fr[kSteps];
 #pragma unroll
-    for (int s2 = 0; s2 < KPF; ++s2) fr[s2] = *(const bf16x8_t *)(kl + 16 * swz(r, 2 * s2 + hb));
+    for (int s2 = 0; s2 < KPF; ++s2) fr[s2] = rdk(s2);
 #pragma unroll
     for (int s2 = 0; s2 < kSteps; ++s2) {
-      if (s2 + KPF < kSteps)
-        fr[s2 + KPF] = *(const bf16x8_t *)(kl + 16 * swz(r, 2 * (s2 + KPF) + hb));
+      if (s2 + KPF < kSteps) fr[s2 + KPF] = rdk(s2 + KPF);
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s2], qf[s2], sacc, 0, 0, 0);
       if ((s2 & 1) && next_tile >= 0) issue_one(next_tile, st ^ 1, s2 >> 1, next_pages);
     }
@@ -241,8 +274,8 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
       const int key_step = 2 * (s2 < 2 ? kh : kh ^ 1) + (s2 & 1);  // keys 16 key_step ..
       const int r0 = 16 * key_step + vrow;
       const int c = 4 * (kDvBlocks * kh + db) + vcb;  // logical chunk (< 64)
-      const char *p0 = vl + r0 * kRowBytes + 16 * (c ^ (r0 & 15));
-      const char *p1 = vl + (r0 + 8) * kRowBytes + 16 * (c ^ ((r0 + 8) & 15));
+      const char *p0 = vl + r0 * kLatBytes + 16 * (c ^ lat_swz(r0));
+      const char *p1 = vl + (r0 + 8) * kLatBytes + 16 * (c ^ lat_swz(r0 + 8));
       const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
       const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
       return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
