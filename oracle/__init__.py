@@ -56,6 +56,7 @@ class _Unit(ctypes.Structure):
         ("q", ctypes.c_void_p),
         ("k", ctypes.c_void_p),
         ("v", ctypes.c_void_p),
+        ("row_first", ctypes.c_void_p),
         ("row_keys", ctypes.c_void_p),
         ("k_begin", ctypes.c_int),
         ("k_end", ctypes.c_int),
@@ -75,16 +76,17 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB_PATH):
+            if not os.path.exists(_LIB_PATH) or \
+                    os.path.getmtime(_SRC) > os.path.getmtime(_LIB_PATH):
                 build()
             lib = ctypes.CDLL(_LIB_PATH)
             P = ctypes.c_void_p
             I = ctypes.c_int
             D = ctypes.c_double
-            lib.oracle_dense_rows.argtypes = [I, I, I, I, P, P, P, P, D, P, P]
+            lib.oracle_dense_rows.argtypes = [I, I, I, I, P, P, P, P, P, D, P, P]
             lib.oracle_dense_rows.restype = I
-            lib.oracle_blasst_rows.argtypes = [I, I, I, P, P, P, P, I, I, I, D, D, P, P, P, P,
-                                               P, P, P, P, I, P]
+            lib.oracle_blasst_rows.argtypes = [I, I, I, P, P, P, P, P, I, I, I, D, D, P, P, P,
+                                               P, P, P, P, P, I, P]
             lib.oracle_blasst_rows.restype = I
             lib.oracle_combine.argtypes = [I, I, I, P, P, P, P]
             lib.oracle_combine.restype = I
@@ -122,32 +124,41 @@ def _check(rc: int, what: str):
 # ----------------------------------------------------------------------------------------------
 # Row-block level entry points
 # ----------------------------------------------------------------------------------------------
-def dense_rows(q, k, v, row_keys, scale: float):
+def _rows_i32(x):
+    return None if x is None else np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def dense_rows(q, k, v, row_keys, scale: float, row_first=None):
     """Dense softmax attention of a block of rows (q: R x d_qk, k: N x d_qk, v: N x d_v).
 
-    Row r attends to keys [0, row_keys[r]). Returns (O [R, d_v], LSE [R]) in float64.
+    Row r attends to keys [row_first[r], row_keys[r]) (row_first None: from 0). Returns
+    (O [R, d_v], LSE [R]) in float64.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
-    rk = np.ascontiguousarray(np.asarray(row_keys, dtype=np.int32))
+    rk = _rows_i32(row_keys)
+    rf = _rows_i32(row_first)
     R, dqk = q.shape
     N, dv = v.shape
     o = np.zeros((R, dv))
     lse = np.zeros(R)
-    _check(_load().oracle_dense_rows(R, N, dqk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(rk),
+    _check(_load().oracle_dense_rows(R, N, dqk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(rf) if rf is not None else None, _ptr(rk),
                                      float(scale), _ptr(o), _ptr(lse)), "oracle_dense_rows")
     return o, lse
 
 
 def blasst_rows(q, k, v, row_keys, k_begin: int, k_end: int, block_c: int, scale: float,
-                lam: float, forced=None):
-    """Tiled BLASST loop of one row block over keys [k_begin, k_end) (see blasst_oracle.c).
+                lam: float, forced=None, row_first=None):
+    """Tiled BLASST loop of one row block over keys [k_begin, k_end) (see blasst_oracle.c);
+    row r sees keys [row_first[r], row_keys[r]) (row_first None: from 0).
 
     Returns a dict with o, lse, m (final running max), l (final running sum), visited, skipped,
     tile_status and tile_margin (one entry per tile of the range). ``forced``: optional per-tile
     decisions (TILE_SKIPPED = skip) imposed instead of the test.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
-    rk = np.ascontiguousarray(np.asarray(row_keys, dtype=np.int32))
+    rk = _rows_i32(row_keys)
+    rf = _rows_i32(row_first)
     R, dqk = q.shape
     dv = v.shape[1]
     n_tiles = max(0, -(-(k_end - k_begin) // block_c))
@@ -164,7 +175,8 @@ def blasst_rows(q, k, v, row_keys, k_begin: int, k_end: int, block_c: int, scale
         fz = np.ascontiguousarray(np.asarray(forced, dtype=np.uint8)[:n_tiles])
         if fz.shape[0] < n_tiles:
             raise ValueError("forced decisions must cover every tile of the range")
-    rc = _load().oracle_blasst_rows(R, dqk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(rk), int(k_begin),
+    rc = _load().oracle_blasst_rows(R, dqk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(rf) if rf is not None else None, _ptr(rk), int(k_begin),
                                     int(k_end), int(block_c), float(scale), float(lam), _ptr(o),
                                     _ptr(lse), _ptr(m), _ptr(l), ctypes.byref(vis),
                                     ctypes.byref(sk), _ptr(ts), _ptr(tm), n_tiles,
@@ -222,7 +234,7 @@ class _Batch:
         self.entries = []  # (key, split index, arrays)
         self.bytes = 0
 
-    def add(self, key, split, q, k, v, row_keys, k_begin, k_end, forced=None):
+    def add(self, key, split, q, k, v, row_keys, k_begin, k_end, forced=None, row_first=None):
         R = q.shape[0]
         n_tiles = max(0, -(-(k_end - k_begin) // self.block_c))
         if forced is not None:
@@ -233,19 +245,21 @@ class _Batch:
         lse = np.zeros(R)
         ts = np.zeros(max(n_tiles, 1), dtype=np.uint8)
         tm = np.zeros(max(n_tiles, 1))
-        rk = np.ascontiguousarray(np.asarray(row_keys, dtype=np.int32))
-        self.keep.append((q, k, v, rk, forced))
-        self.entries.append((key, split, R, q, k, v, rk, k_begin, k_end, o, lse, ts, tm, n_tiles,
-                             forced))
+        rk = _rows_i32(row_keys)
+        rf = _rows_i32(row_first)
+        self.keep.append((q, k, v, rk, rf, forced))
+        self.entries.append((key, split, R, q, k, v, rf, rk, k_begin, k_end, o, lse, ts, tm,
+                             n_tiles, forced))
 
     def run(self, sink):
         if not self.entries:
             return
         units = (_Unit * len(self.entries))()
         for i, e in enumerate(self.entries):
-            key, split, R, q, k, v, rk, kb, ke, o, lse, ts, tm, nt, fz = e
+            key, split, R, q, k, v, rf, rk, kb, ke, o, lse, ts, tm, nt, fz = e
             u = units[i]
             u.n_rows, u.q, u.k, u.v, u.row_keys = R, q.ctypes.data, k.ctypes.data, v.ctypes.data, rk.ctypes.data
+            u.row_first = rf.ctypes.data if rf is not None else None
             u.k_begin, u.k_end = kb, ke
             u.o, u.lse = o.ctypes.data, lse.ctypes.data
             u.tile_status, u.tile_margin, u.max_tiles = ts.ctypes.data, tm.ctypes.data, nt
@@ -260,7 +274,7 @@ class _Batch:
                                          float(self.lam), int(self.threads))
         _check(rc, "oracle batch")
         for i, e in enumerate(self.entries):
-            key, split, R, q, k, v, rk, kb, ke, o, lse, ts, tm, nt, _ = e
+            key, split, R, q, k, v, rf, rk, kb, ke, o, lse, ts, tm, nt, _ = e
             sink(key, split, UnitResult(o, lse, units[i].visited, units[i].skipped,
                                         ts[:nt].copy(), tm[:nt].copy()))
         self.keep.clear()
@@ -273,8 +287,11 @@ def _as_shape(x):
 
 def prefill(q, k, v, *, causal: bool, block_r: int, block_c: int, scale: float, lam: float,
             units=None, threads: int = 0, dense: bool = False, forced=None,
-            budget_bytes: int = 1 << 30) -> CallResult:
+            budget_bytes: int = 1 << 30, window: int = 0) -> CallResult:
     """Oracle of a prefill call. q: [B, Lq, Hq, d_qk], k: [B, Lkv, Hkv, d_qk], v: [B, Lkv, Hkv, d_v].
+
+    window > 0 (causal only): query position i sees keys i - window + 1 .. i (a sliding window
+    of window keys ending at the row); tiles before every row's window are not visited.
 
     units: iterable of (b, h, qb) or None for every unit. dense=True evaluates the dense
     definition instead of the tiled loop (tile fields are then empty). forced: optional dict
@@ -287,6 +304,8 @@ def prefill(q, k, v, *, causal: bool, block_r: int, block_c: int, scale: float, 
         raise ValueError("Hq must be a multiple of Hkv")
     if causal and Lq != Lkv:
         raise ValueError("causal prefill needs Lq == Lkv")
+    if window < 0 or (window and not causal):
+        raise ValueError("a sliding window needs causal prefill and window > 0")
     grp = Hq // Hkv
     n_qb = -(-Lq // block_r)
     if units is None:
@@ -315,34 +334,47 @@ def prefill(q, k, v, *, causal: bool, block_r: int, block_c: int, scale: float, 
             row_keys = [min(p + 1, Lkv) for p in range(r0, r1)]
         else:
             row_keys = [Lkv] * (r1 - r0)
+        row_first = [max(0, p - window + 1) for p in range(r0, r1)] if window else None
         batch.add((b, h, qb), 0, qf, kf, vf, row_keys, 0, Lkv,
-                  forced.get((b, h, qb)) if forced else None)
+                  forced.get((b, h, qb)) if forced else None, row_first)
     batch.run(sink)
     return result
 
 
-def split_ranges(kv_len: int, max_kv_len: int, block_c: int, num_splits: int):
-    """Key ranges of the splits of one sequence: equal runs of whole tiles, cut on max_kv_len."""
+def window_first_key(kv_len: int, window: int) -> int:
+    """First key a decode query at position kv_len - 1 sees: kv_len - window, or 0 (no window)."""
+    return max(0, kv_len - window) if window else 0
+
+
+def split_ranges(kv_len: int, max_kv_len: int, block_c: int, num_splits: int, window: int = 0):
+    """Key ranges of the splits of one sequence: equal runs of whole tiles. Without a window the
+    runs cut the tiles of max_kv_len from tile 0; with one they cut the at most
+    ceil(window / block_c) + 1 tiles a window can touch, from the tile holding the sequence's
+    first visible key."""
     n_tiles = -(-max_kv_len // block_c)
-    per = -(-n_tiles // num_splits) if n_tiles else 0
+    span = min(n_tiles, -(-window // block_c) + 1) if window else n_tiles
+    per = -(-span // num_splits) if span else 0
+    base = window_first_key(kv_len, window) // block_c * block_c
     out = []
     for s in range(num_splits):
-        a = min(s * per * block_c, kv_len)
-        e = min((s + 1) * per * block_c, kv_len)
+        a = min(base + s * per * block_c, kv_len)
+        e = min(base + (s + 1) * per * block_c, kv_len)
         out.append((a, e))
     return out
 
 
 def decode(q, k, v, *, kv_len=None, block_r: int, block_c: int, num_splits: int = 1,
            scale: float, lam: float, units=None, threads: int = 0, dense: bool = False,
-           forced=None, budget_bytes: int = 1 << 30) -> CallResult:
+           forced=None, budget_bytes: int = 1 << 30, window: int = 0) -> CallResult:
     """Oracle of a decode call (one query token per sequence).
 
     q: [B, Hq, d_qk], k: [B, L, Hkv, d_qk], v: [B, L, Hkv, d_v]; kv_len: per-sequence lengths
     (None = all L). units: iterable of (b, g, rb) or None for all. Each unit's splits are merged
-    by log-sum-exp; visited/skipped and tile arrays cover all of its splits. forced: optional
-    dict unit -> decisions for the unit's tiles 0, 1, ... (absolute tile index), imposed instead
-    of the test.
+    by log-sum-exp; visited/skipped cover all of its splits and the tile arrays are indexed by
+    absolute tile (ceil(max(kv_len) / block_c) entries; tiles no split visits are "not
+    visited"). forced: optional dict unit -> decisions for the unit's tiles 0, 1, ... (absolute
+    tile index), imposed instead of the test. window > 0: the query (at position kv_len - 1)
+    sees only keys kv_len - window .. kv_len - 1 (see split_ranges for the splits).
     """
     B, Hq, dqk = _as_shape(q)
     _, L, Hkv, _ = _as_shape(k)
@@ -358,7 +390,10 @@ def decode(q, k, v, *, kv_len=None, block_r: int, block_c: int, num_splits: int 
     if units is None:
         units = [(b, g, rb) for b in range(B) for g in range(Hkv) for rb in range(n_rb)]
     units = sorted(set(tuple(int(x) for x in u) for u in units))
+    if window < 0:
+        raise ValueError("window must be >= 0")
     parts: dict = {}
+    starts: dict = {}  # unit -> first absolute tile of each split's range
 
     def sink(key, split, ur):
         parts.setdefault(key, {})[split] = ur
@@ -377,25 +412,36 @@ def decode(q, k, v, *, kv_len=None, block_r: int, block_c: int, num_splits: int 
         h0 = g * grp + rb * block_r
         h1 = min(g * grp + (rb + 1) * block_r, (g + 1) * grp)
         qf = _f64(q[b, h0:h1, :])
-        ranges = [(0, kv_len[b])] if (dense or num_splits == 1) else \
-            split_ranges(kv_len[b], max_len, block_c, num_splits)
+        first = window_first_key(kv_len[b], window)
+        if dense or num_splits == 1:
+            ranges = [(first // block_c * block_c, kv_len[b])]
+        else:
+            ranges = split_ranges(kv_len[b], max_len, block_c, num_splits, window)
         fu = forced.get((b, g, rb)) if forced else None
         for s, (a, e) in enumerate(ranges):
             fs = None if fu is None else np.asarray(fu)[a // block_c:]
-            batch.add((b, g, rb), s, qf, kf, vf, [kv_len[b]] * (h1 - h0), a, e, fs)
+            batch.add((b, g, rb), s, qf, kf, vf, [kv_len[b]] * (h1 - h0), a, e, fs,
+                      [first] * (h1 - h0) if window else None)
+        starts.setdefault((b, g, rb), [a // block_c for a, _ in ranges])
     batch.run(sink)
 
+    n_all = -(-max_len // block_c)
     result = CallResult()
     for key, sp in parts.items():
         idx = sorted(sp)
+        ts = np.full(n_all, TILE_NOT_VISITED, dtype=np.uint8)
+        tm = np.full(n_all, -np.inf)
+        for i in idx:
+            t0 = starts[key][i]
+            nt = len(sp[i].tile_status)
+            ts[t0:t0 + nt] = sp[i].tile_status
+            tm[t0:t0 + nt] = sp[i].tile_margin
         if len(idx) == 1:
-            result.units[key] = sp[idx[0]]
-            continue
-        o, lse = combine(np.stack([sp[i].o for i in idx]), np.stack([sp[i].lse for i in idx]))
-        result.units[key] = UnitResult(
-            o, lse, sum(sp[i].visited for i in idx), sum(sp[i].skipped for i in idx),
-            np.concatenate([sp[i].tile_status for i in idx]),
-            np.concatenate([sp[i].tile_margin for i in idx]))
+            o, lse = sp[idx[0]].o, sp[idx[0]].lse
+        else:
+            o, lse = combine(np.stack([sp[i].o for i in idx]), np.stack([sp[i].lse for i in idx]))
+        result.units[key] = UnitResult(o, lse, sum(sp[i].visited for i in idx),
+                                       sum(sp[i].skipped for i in idx), ts, tm)
     return result
 
 

@@ -59,34 +59,37 @@ static double dot(const double *a, const double *b, int n) {
 /*
  * Dense softmax attention for a block of query rows: the definition in [HG] "Why Standard
  * Attention is IO-Bound", written out with the usual max subtraction.
- *   s_rk  = scale * <q_r, k_k>           for keys k < row_keys[r]
+ *   s_rk  = scale * <q_r, k_k>           for keys row_first[r] <= k < row_keys[r]
  *   O_r   = sum_k exp(s_rk - M_r) v_k / sum_k exp(s_rk - M_r),   M_r = max_k s_rk
  *   LSE_r = M_r + ln sum_k exp(s_rk - M_r)
- * A row with no visible key gets O_r = 0 and LSE_r = -inf.
+ * A row with no visible key gets O_r = 0 and LSE_r = -inf. row_first may be NULL (every row's
+ * first visible key is 0); a sliding window of W keys ending at the row's position gives
+ * row_first = position - W + 1.
  *
  * q: n_rows x d_qk, k: n_keys x d_qk, v: n_keys x d_v, o: n_rows x d_v, lse: n_rows.
  */
 int oracle_dense_rows(int n_rows, int n_keys, int d_qk, int d_v, const double *q,
-                      const double *k, const double *v, const int *row_keys, double scale,
-                      double *o, double *lse) {
+                      const double *k, const double *v, const int *row_first,
+                      const int *row_keys, double scale, double *o, double *lse) {
   if (n_rows < 0 || n_keys < 0 || d_qk <= 0 || d_v <= 0) return ORACLE_BAD_ARG;
   double *s = (double *)malloc(sizeof(double) * (n_keys > 0 ? n_keys : 1));
   if (!s) return ORACLE_NO_MEMORY;
   for (int r = 0; r < n_rows; ++r) {
     int nk = row_keys[r] < n_keys ? row_keys[r] : n_keys;
+    int j0 = row_first && row_first[r] > 0 ? row_first[r] : 0;
     double *orow = o + (size_t)r * d_v;
     for (int c = 0; c < d_v; ++c) orow[c] = 0.0;
-    if (nk <= 0) {
+    if (nk <= j0) {
       lse[r] = -INFINITY;
       continue;
     }
     double mx = -INFINITY;
-    for (int j = 0; j < nk; ++j) {
+    for (int j = j0; j < nk; ++j) {
       s[j] = scale * dot(q + (size_t)r * d_qk, k + (size_t)j * d_qk, d_qk);
       if (s[j] > mx) mx = s[j];
     }
     double z = 0.0;
-    for (int j = 0; j < nk; ++j) {
+    for (int j = j0; j < nk; ++j) {
       double p = exp(s[j] - mx);
       z += p;
       const double *vj = v + (size_t)j * d_v;
@@ -103,7 +106,8 @@ int oracle_dense_rows(int n_rows, int n_keys, int d_qk, int d_v, const double *q
  * The tiled BLASST loop for one block of query rows (one "tile row" of B_r rows) over the key
  * range [k_begin, k_end), in tiles of block_c keys starting at k_begin, visited in ascending
  * order ([HG] "FlashAttention Tiling Strategy"). Keys are indexed absolutely: k and v hold at
- * least k_end rows. Row r sees keys with index < row_keys[r].
+ * least k_end rows. Row r sees keys with row_first[r] <= index < row_keys[r] (row_first NULL:
+ * from index 0).
  *
  * Per tile ([SS] "Algorithm"; [BL] Eq. 2):
  *   1. scores s_rk = scale * <q_r, k_k>; keys the row cannot see score -inf;
@@ -127,7 +131,8 @@ int oracle_dense_rows(int n_rows, int n_keys, int d_qk, int d_v, const double *q
  * max then stays where it was, as in the kernel.
  */
 int oracle_blasst_rows(int n_rows, int d_qk, int d_v, const double *q, const double *k,
-                       const double *v, const int *row_keys, int k_begin, int k_end,
+                       const double *v, const int *row_first, const int *row_keys,
+                       int k_begin, int k_end,
                        int block_c, double scale, double lambda, double *o, double *lse,
                        double *row_max, double *row_sum, long long *visited, long long *skipped,
                        unsigned char *tile_status, double *tile_margin, int max_tiles,
@@ -163,7 +168,7 @@ int oracle_blasst_rows(int n_rows, int d_qk, int d_v, const double *q, const dou
     /* A tile that no row can see is not visited. */
     int seen = 0;
     for (int r = 0; r < n_rows; ++r)
-      if (row_keys[r] > t0) seen = 1;
+      if (row_keys[r] > t0 && (!row_first || row_first[r] < t1)) seen = 1;
     if (!seen) {
       if (tile_status && tile < max_tiles) tile_status[tile] = ORACLE_TILE_NOT_VISITED;
       if (tile_margin && tile < max_tiles) tile_margin[tile] = -INFINITY;
@@ -176,9 +181,10 @@ int oracle_blasst_rows(int n_rows, int d_qk, int d_v, const double *q, const dou
     for (int r = 0; r < n_rows; ++r) {
       double *sr = s + (size_t)r * block_c;
       int vis_end = row_keys[r] < t1 ? row_keys[r] : t1;
+      int vis_begin = row_first ? row_first[r] : 0;
       mt[r] = -INFINITY;
       for (int kk = t0; kk < t1; ++kk) {
-        if (kk < vis_end) {
+        if (kk >= vis_begin && kk < vis_end) {
           sr[kk - t0] = scale * dot(q + (size_t)r * d_qk, k + (size_t)kk * d_qk, d_qk);
           if (sr[kk - t0] > mt[r]) mt[r] = sr[kk - t0];
         } else {
@@ -288,6 +294,7 @@ typedef struct {
   const double *q;
   const double *k;
   const double *v;
+  const int *row_first; /* may be NULL */
   const int *row_keys;
   int k_begin, k_end;
   double *o;
@@ -314,7 +321,8 @@ int oracle_blasst_batch(int n_units, oracle_unit *units, int d_qk, int d_v, int 
     oracle_unit *un = &units[u];
     un->visited = 0;
     un->skipped = 0;
-    un->status = oracle_blasst_rows(un->n_rows, d_qk, d_v, un->q, un->k, un->v, un->row_keys,
+    un->status = oracle_blasst_rows(un->n_rows, d_qk, d_v, un->q, un->k, un->v, un->row_first,
+                                    un->row_keys,
                                     un->k_begin, un->k_end, block_c, scale, lambda, un->o,
                                     un->lse, NULL, NULL, &un->visited, &un->skipped,
                                     un->tile_status, un->tile_margin, un->max_tiles,
@@ -334,7 +342,7 @@ int oracle_dense_batch(int n_units, oracle_unit *units, int d_qk, int d_v, doubl
   for (int u = 0; u < n_units; ++u) {
     oracle_unit *un = &units[u];
     un->status = oracle_dense_rows(un->n_rows, un->k_end, d_qk, d_v, un->q, un->k, un->v,
-                                   un->row_keys, scale, un->o, un->lse);
+                                   un->row_first, un->row_keys, scale, un->o, un->lse);
   }
   for (int u = 0; u < n_units; ++u)
     if (units[u].status != ORACLE_OK) worst = units[u].status;

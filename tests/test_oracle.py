@@ -28,15 +28,18 @@ import oracle
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _masked_scores(q, k, row_keys, scale):
+def _masked_scores(q, k, row_keys, scale, row_first=None):
     s = scale * (q @ k.T)
-    mask = np.arange(k.shape[0])[None, :] >= np.asarray(row_keys)[:, None]
+    idx = np.arange(k.shape[0])[None, :]
+    mask = idx >= np.asarray(row_keys)[:, None]
+    if row_first is not None:
+        mask |= idx < np.asarray(row_first)[:, None]
     s = np.where(mask, -np.inf, s)
     return s
 
 
-def _library_attention(q, k, v, row_keys, scale):
-    s = _masked_scores(q, k, row_keys, scale)
+def _library_attention(q, k, v, row_keys, scale, row_first=None):
+    s = _masked_scores(q, k, row_keys, scale, row_first)
     return softmax(s, axis=1) @ v, logsumexp(s, axis=1)
 
 
@@ -50,10 +53,10 @@ def _clustered_rows(rng, n_rows, n_keys, d, d_v, beta, cluster=16):
     return q, k, v
 
 
-def _closed_form(q, k, v, row_keys, scale, lam, block_c, k_begin=0, k_end=None):
+def _closed_form(q, k, v, row_keys, scale, lam, block_c, k_begin=0, k_end=None, row_first=None):
     """Kept set from prefix maxima of tile maxima; output = softmax over the kept keys."""
     n_keys = k.shape[0] if k_end is None else k_end
-    s = _masked_scores(q, k[:n_keys], row_keys, scale)[:, k_begin:n_keys]
+    s = _masked_scores(q, k[:n_keys], row_keys, scale, row_first)[:, k_begin:n_keys]
     n = s.shape[1]
     tiles = [(a, min(a + block_c, n)) for a in range(0, n, block_c)]
     tmax = np.stack([s[:, a:e].max(axis=1) for a, e in tiles], axis=1)  # rows x tiles
@@ -426,3 +429,111 @@ def test_sparsity_curve_from_one_pass_equals_separate_runs():
         assert vis == n_vis
         assert frac == sk / vis, (lam, frac, sk / vis)
     assert curve == sorted(curve) and 0 < curve[-2] < 1
+
+
+# ------------------------------------------------------------------------------------------
+# Sliding window (the talk notes' Q&A: windowed attention as structured sparsity): a row sees
+# keys [row_first, row_keys). Tiles before every row's window are not visited.
+# ------------------------------------------------------------------------------------------
+def test_window_dense_rows_match_scipy():
+    rng = np.random.default_rng(71)
+    n_rows, n_keys, d, dv = 7, 90, 16, 12
+    q = rng.standard_normal((n_rows, d))
+    k = rng.standard_normal((n_keys, d))
+    v = rng.standard_normal((n_keys, dv))
+    row_keys = [90, 90, 60, 41, 41, 5, 90]
+    row_first = [0, 30, 59, 1, 40, 0, 89]
+    o, lse = oracle.dense_rows(q, k, v, row_keys, 0.3, row_first=row_first)
+    o_ref, lse_ref = _library_attention(q, k, v, row_keys, 0.3, row_first)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_window_streaming_matches_closed_form(seed):
+    rng = np.random.default_rng(300 + seed)
+    n_rows = int(rng.integers(1, 7))
+    n_keys = int(rng.integers(60, 300))
+    block_c = int(rng.choice([8, 16, 33]))
+    q, k, v = _clustered_rows(rng, n_rows, n_keys, 16, 6, beta=8.0)
+    row_keys = sorted(rng.integers(n_keys // 2, n_keys + 1, size=n_rows).tolist())
+    width = int(rng.integers(5, n_keys // 2))
+    row_first = [max(0, e - width) for e in row_keys]
+    for lam in (0.0, 1e-3, 0.1, 1.0):
+        r = oracle.blasst_rows(q, k, v, row_keys, 0, n_keys, block_c, 0.25, lam,
+                               row_first=row_first)
+        cf = _closed_form(q, k, v, row_keys, 0.25, lam, block_c, row_first=row_first)
+        vis = cf["visited"]
+        first_tile = min(row_first) // block_c
+        assert not vis[:first_tile].any()  # tiles before every window are not visited
+        np.testing.assert_array_equal(r["tile_status"][vis] == oracle.TILE_SKIPPED,
+                                      cf["skipped"][vis])
+        assert np.all(r["tile_status"][~vis] == oracle.TILE_NOT_VISITED)
+        np.testing.assert_allclose(r["tile_margin"][vis], cf["margin"][vis], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r["o"], cf["o"], rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(r["lse"], cf["lse"], rtol=1e-12, atol=1e-12)
+
+
+def test_window_prefill_lambda_zero_matches_torch_sdpa_with_band_mask():
+    from flashattention_softmax_threshold_amd.inputs import prefill_inputs
+
+    B, L, Hq, Hkv, d, W = 1, 150, 4, 2, 16, 40
+    q, k, v = prefill_inputs(B=B, L=L, Hq=Hq, Hkv=Hkv, d=d, cluster_len=32, dtype=torch.float32,
+                             seed=9, beta=4.0, sinks=8)
+    res = oracle.prefill(q, k, v, causal=True, block_r=32, block_c=16, scale=1 / math.sqrt(d),
+                         lam=0.0, window=W)
+    i = torch.arange(L)
+    allowed = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - W)
+    qt, kt, vt = (torch.as_tensor(x.numpy(), dtype=torch.float64).transpose(1, 2) for x in (q, k, v))
+    kt, vt = kt.repeat_interleave(Hq // Hkv, dim=1), vt.repeat_interleave(Hq // Hkv, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed)
+    ref = ref.transpose(1, 2).numpy()
+    for (b, h, qb), u in res.units.items():
+        r0 = qb * 32
+        r1 = r0 + u.o.shape[0]
+        np.testing.assert_allclose(u.o, ref[b, r0:r1, h], rtol=1e-10, atol=1e-11)
+        # Visited: the tiles meeting [r0 - W + 1, r1 - 1].
+        assert u.visited == (r1 - 1) // 16 - max(0, r0 - W + 1) // 16 + 1
+        assert np.all(u.tile_status[:max(0, r0 - W + 1) // 16] == oracle.TILE_NOT_VISITED)
+
+
+def test_window_decode_lambda_zero_matches_softmax_with_lengths_and_splits():
+    from flashattention_softmax_threshold_amd.inputs import decode_inputs
+
+    B, Hq, Hkv, L, d, dv, W = 3, 8, 2, 300, 16, 12, 70
+    kv_len = [300, 50, 129]
+    q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=Hkv, L=L, d_qk=d, d_v=dv, cluster_len=50,
+                                 dtype=torch.float32, seed=15, beta=3.0, kv_len=kv_len)
+    for splits in (1, 2, 5):
+        res = oracle.decode(q, k, v, kv_len=kvl, block_r=4, block_c=32, num_splits=splits,
+                            scale=0.25, lam=0.0, window=W)
+        for (b, g, rb), u in res.units.items():
+            n = kv_len[b]
+            a = max(0, n - W)
+            for i, h in enumerate(range(g * 4, g * 4 + 4)):
+                s = 0.25 * (k[b, a:n, g].double() @ q[b, h].double())
+                ref = torch.softmax(s, 0) @ v[b, a:n, g].double()
+                np.testing.assert_allclose(u.o[i], ref.numpy(), rtol=1e-11, atol=1e-12)
+                np.testing.assert_allclose(u.lse[i], torch.logsumexp(s, 0).item(), rtol=1e-12)
+            assert u.visited == (n - 1) // 32 - a // 32 + 1
+            assert np.all(u.tile_status[:a // 32] == oracle.TILE_NOT_VISITED)
+
+
+def test_window_covering_everything_equals_no_window():
+    from flashattention_softmax_threshold_amd.inputs import decode_inputs, prefill_inputs
+
+    q, k, v = prefill_inputs(B=1, L=100, Hq=2, Hkv=1, d=16, cluster_len=20, dtype=torch.float32,
+                             seed=4, beta=8.0, sinks=4)
+    kw = dict(causal=True, block_r=32, block_c=16, scale=0.25, lam=0.05)
+    a, b = oracle.prefill(q, k, v, **kw), oracle.prefill(q, k, v, window=100, **kw)
+    qd, kd, vd, kvl = decode_inputs(B=2, Hq=4, Hkv=1, L=200, d_qk=16, d_v=16, cluster_len=40,
+                                    dtype=torch.float32, seed=6, beta=8.0, kv_len=[200, 77])
+    kwd = dict(kv_len=kvl, block_r=4, block_c=32, num_splits=1, scale=0.25, lam=0.05)
+    c, e = oracle.decode(qd, kd, vd, **kwd), oracle.decode(qd, kd, vd, window=200, **kwd)
+    for x, y in ((a, b), (c, e)):
+        assert x.units.keys() == y.units.keys() and x.skipped > 0
+        for key in x.units:
+            ux, uy = x.units[key], y.units[key]
+            assert np.array_equal(ux.o, uy.o) and np.array_equal(ux.lse, uy.lse)
+            assert np.array_equal(ux.tile_status, uy.tile_status)
+            assert ux.visited == uy.visited and ux.skipped == uy.skipped
