@@ -47,6 +47,7 @@ MLA_BETA = 16.0
 DIT_BETA = 4.0  # the Video-DiT generator's centre gain: skip fraction in the pages' range
 WAN_A, WAN_B = 2822.6209952221557, 4.388250623520793  # "Skip-Softmax calibration config"
 PAGE_SIZES = (16, 64)  # paged-cache points of the GQA decode measurement
+WINDOW_PREFILL, WINDOW_DECODE = 2048, 4096  # sliding-window points (keys)
 CALIB_BETA = 16.0  # smoother score spread than the headline's, so the swept curve has a slope
 
 
@@ -57,7 +58,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="same as --part prefill")
-    ap.add_argument("--part", choices=("all", "prefill", "decode", "mla", "calib", "dit"),
+    ap.add_argument("--part", choices=("all", "prefill", "decode", "mla", "calib", "dit",
+                                       "window"),
                     default="all",
                     help="prefill: the headline call only; decode / mla: that decode only "
                          "(profiling runs isolate one kernel this way)")
@@ -440,6 +442,72 @@ def _dit_part(F, torch, args, dev, stream, out):
     del q, k, v
 
 
+def _window_part(F, torch, args, dev, stream, out):
+    """Sliding windows on the causal prefill and GQA decode workloads (the talk notes' Q&A:
+    windowed attention as structured sparsity). lambda = a / W: the window, not the context,
+    is the number of keys a query's softmax spreads over."""
+    from flashattention_softmax_threshold_amd.inputs import decode_inputs, prefill_inputs
+
+    P, D = PREFILL, DECODE
+    L, d, Hq, W = P["L"], P["d"], P["Hq"], WINDOW_PREFILL
+    q, k, v = prefill_inputs(B=P["B"], L=L, Hq=Hq, Hkv=P["Hkv"], d=d,
+                             cluster_len=P["cluster_len"], dtype=torch.bfloat16, device=dev,
+                             seed=P["seed"], beta=PREFILL_BETA, sinks=P["sinks"])
+    br, bc = F.blasst_prefill_tiles(q, k)
+    o = torch.empty_like(q)
+    tile_flops = 2.0 * br * bc * d
+    dense_flops = 4.0 * Hq * d * sum(min(i + 1, W) for i in range(L))
+    pts = []
+    ms0 = None
+    for a in (0.0, 16.0):
+        lam = a / W
+        ms = _time_calls(lambda: F.blasst_attn_prefill(q, k, v, causal=True, lam=lam, o=o,  # noqa
+                                                       window=W, stream=stream),
+                         args.steps, args.warmup, stream)
+        cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+        F.blasst_attn_prefill(q, k, v, causal=True, lam=lam, counters=cnt, window=W)
+        torch.cuda.synchronize()
+        vis, sk = (int(x) for x in cnt.cpu().tolist())
+        ms0 = ms if a == 0.0 else ms0
+        ex = tile_flops * (2 * vis - sk) / (ms * 1e-3) / 1e12
+        pts.append({"lambda": f"{a:g}/W", "ms": ms, "skip_fraction": sk / vis,
+                    "dense_tflops": dense_flops / (ms * 1e-3) / 1e12, "executed_tflops": ex,
+                    "mfma_frac": ex / BF16_PEAK_TFLOPS, "speedup_vs_lambda0": ms0 / ms})
+        _progress(f"window prefill a={a:g}: {ms:.4f} ms")
+    out["window_prefill"] = {"workload": f"causal GQA prefill B1 Hq32/Hkv8 L8192 d128 bf16, "
+                                         f"window {W}, tile {br}x{bc}", "points": pts}
+    del q, k, v
+
+    Wd = WINDOW_DECODE
+    qd, kd, vd, kvl = decode_inputs(B=D["B"], Hq=D["Hq"], Hkv=D["Hkv"], L=D["L"], d_qk=D["d"],
+                                    d_v=D["d"], cluster_len=D["cluster_len"],
+                                    dtype=torch.bfloat16, device=dev, seed=D["seed"],
+                                    beta=DECODE_BETA)
+    od = torch.empty((D["B"], D["Hq"], D["d"]), dtype=torch.bfloat16, device=dev)
+    _, bcd, sd = F.blasst_decode_plan(qd, kd, vd, window=Wd)
+    wsd = torch.empty(max(F.blasst_decode_workspace_size(qd, kd, vd, window=Wd), 1),
+                      dtype=torch.uint8, device=dev)
+    tile_bytes = bcd * D["d"] * 2
+    dpts = []
+    for a in (0.0, 16.0):
+        lam = a / Wd
+        ms = _time_calls(lambda: F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=lam, o=od,  # noqa
+                                                      workspace=wsd, window=Wd, stream=stream),
+                         args.steps, args.warmup, stream)
+        cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+        F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=lam, o=od, counters=cnt, workspace=wsd,
+                             window=Wd)
+        torch.cuda.synchronize()
+        vis, sk = (int(x) for x in cnt.cpu().tolist())
+        nbytes = tile_bytes * (2 * vis - sk) + qd.numel() * 2 + od.numel() * 2
+        dpts.append({"lambda": f"{a:g}/W", "ms": ms, "skip_fraction": sk / vis,
+                     "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                     "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        _progress(f"window decode a={a:g}: {ms:.4f} ms")
+    out["window_decode"] = {"workload": f"GQA decode B64 Hq32/Hkv8 KV32768 d128 bf16, window {Wd}, "
+                                        f"tile 4x{bcd}, {sd} splits", "points": dpts}
+
+
 def _calib_part(F, torch, args, dev, stream, out):
     """Calibration sweep (talk notes, Algorithm 2): one lambda = 0 call per length records the
     tile margins; the skip fraction at every candidate follows from them. Reports the fixed-
@@ -523,6 +591,8 @@ def main():
         _mla_part(F, torch, args, dev, stream, out)
     if args.part in ("all", "dit"):
         _dit_part(F, torch, args, dev, stream, out)
+    if args.part in ("all", "window"):
+        _window_part(F, torch, args, dev, stream, out)
     if args.part in ("all", "calib"):
         _calib_part(F, torch, args, dev, stream, out)
     if headline is not None and not args.no_cpu_baseline:

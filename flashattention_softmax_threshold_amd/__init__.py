@@ -82,6 +82,7 @@ class _PrefillArgs(ctypes.Structure):
         ("lse", ctypes.c_void_p), ("counters", ctypes.c_void_p),
         ("tile_status", ctypes.c_void_p), ("tile_margin", ctypes.c_void_p),
         ("block_r", ctypes.c_int32), ("block_c", ctypes.c_int32),
+        ("window", ctypes.c_int32),
     ]
 
 
@@ -103,6 +104,7 @@ class _DecodeArgs(ctypes.Structure):
         ("block_r", ctypes.c_int32), ("block_c", ctypes.c_int32), ("num_splits", ctypes.c_int32),
         ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
         ("pages_per_seq", ctypes.c_int32),
+        ("window", ctypes.c_int32),
     ]
 
 
@@ -253,7 +255,7 @@ def _stream_handle(stream):
 
 
 def _prefill_args(q, k, v, o, *, causal, lam, softmax_scale, lse, counters, tile_status,
-                  tile_margin, block_r, block_c) -> _PrefillArgs:
+                  tile_margin, block_r, block_c, window=0) -> _PrefillArgs:
     B, Lq, Hq, D = q.shape
     Lkv, Hkv = k.shape[1], k.shape[2]
     a = _PrefillArgs()
@@ -272,6 +274,7 @@ def _prefill_args(q, k, v, o, *, causal, lam, softmax_scale, lse, counters, tile
     a.tile_status = tile_status.data_ptr() if tile_status is not None else 0
     a.tile_margin = tile_margin.data_ptr() if tile_margin is not None else 0
     a.block_r, a.block_c = int(block_r), int(block_c)
+    a.window = int(window)
     return a
 
 
@@ -298,11 +301,12 @@ def _check_tensor(t, name, ndim, device):
 def blasst_attn_prefill(q, k, v, *, causal: bool = False, lam: float = 0.0,
                         softmax_scale: float = 0.0, o=None, lse=None, counters=None,
                         tile_status=None, tile_margin=None, block_r: int = 0, block_c: int = 0,
-                        stream=None):
+                        window: int = 0, stream=None):
     """BLASST prefill on q [B, Lq, Hq, D], k/v [B, Lkv, Hkv, D]; returns o [B, Lq, Hq, D].
 
     lse: optional fp32 [B, Hq, Lq]; counters: optional uint64 (int64) [2] accumulated (visited,
     skipped); tile_status (uint8) / tile_margin (fp32): optional [B, Hq, n_qblocks, n_kvtiles].
+    window: causal sliding window in keys (0 = none).
     """
     import torch
 
@@ -315,7 +319,7 @@ def blasst_attn_prefill(q, k, v, *, causal: bool = False, lam: float = 0.0,
         o = torch.empty(q.shape, dtype=q.dtype, device=dev)
     a = _prefill_args(q, k, v, o, causal=causal, lam=lam, softmax_scale=softmax_scale, lse=lse,
                       counters=counters, tile_status=tile_status, tile_margin=tile_margin,
-                      block_r=block_r, block_c=block_c)
+                      block_r=block_r, block_c=block_c, window=window)
     _check(load_library().blasst_attn_prefill(ctypes.byref(a), _stream_handle(stream)),
            "blasst_attn_prefill")
     return o
@@ -323,7 +327,7 @@ def blasst_attn_prefill(q, k, v, *, causal: bool = False, lam: float = 0.0,
 
 def _decode_args(q, k, v, o, *, kv_len, lam, softmax_scale, lse, counters, tile_status,
                  tile_margin, block_r, block_c, num_splits, block_table=None,
-                 max_kv_len=None) -> _DecodeArgs:
+                 max_kv_len=None, window=0) -> _DecodeArgs:
     B, Hq, Dqk = q.shape
     L, Hkv = k.shape[1], k.shape[2]
     if block_table is not None:  # k, v are page pools [pages, page_size, Hkv, d]
@@ -353,16 +357,17 @@ def _decode_args(q, k, v, o, *, kv_len, lam, softmax_scale, lse, counters, tile_
         a.block_table = block_table.data_ptr()
         a.page_size = int(k.shape[1])
         a.pages_per_seq = int(block_table.shape[1])
+    a.window = int(window)
     return a
 
 
 def blasst_decode_plan(q, k, v, *, block_r: int = 0, block_c: int = 0, num_splits: int = 0,
-                       block_table=None, max_kv_len=None):
+                       block_table=None, max_kv_len=None, window: int = 0):
     """(block_r, block_c, num_splits) a decode call on these tensors uses."""
     a = _decode_args(q, k, v, None, kv_len=None, lam=0.0, softmax_scale=0.0, lse=None,
                      counters=None, tile_status=None, tile_margin=None, block_r=block_r,
                      block_c=block_c, num_splits=num_splits, block_table=block_table,
-                     max_kv_len=max_kv_len)
+                     max_kv_len=max_kv_len, window=window)
     br, bc, s = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
     _check(load_library().blasst_decode_plan(ctypes.byref(a), ctypes.byref(br), ctypes.byref(bc),
                                              ctypes.byref(s)), "blasst_decode_plan")
@@ -370,23 +375,25 @@ def blasst_decode_plan(q, k, v, *, block_r: int = 0, block_c: int = 0, num_split
 
 
 def blasst_decode_workspace_size(q, k, v, *, block_r: int = 0, block_c: int = 0,
-                                 num_splits: int = 0, block_table=None, max_kv_len=None) -> int:
+                                 num_splits: int = 0, block_table=None, max_kv_len=None,
+                                 window: int = 0) -> int:
     a = _decode_args(q, k, v, None, kv_len=None, lam=0.0, softmax_scale=0.0, lse=None,
                      counters=None, tile_status=None, tile_margin=None, block_r=block_r,
                      block_c=block_c, num_splits=num_splits, block_table=block_table,
-                     max_kv_len=max_kv_len)
+                     max_kv_len=max_kv_len, window=window)
     return int(load_library().blasst_decode_workspace_size(ctypes.byref(a)))
 
 
 def blasst_attn_decode(q, k, v, *, kv_len=None, lam: float = 0.0, softmax_scale: float = 0.0,
                        o=None, lse=None, counters=None, tile_status=None, tile_margin=None,
                        block_r: int = 0, block_c: int = 0, num_splits: int = 0, workspace=None,
-                       block_table=None, max_kv_len=None, stream=None):
+                       block_table=None, max_kv_len=None, window: int = 0, stream=None):
     """BLASST decode: q [B, Hq, Dqk], k [B, L, Hkv, Dqk], v [B, L, Hkv, Dv] (v may be a view of
     k's first Dv columns: MLA shape); kv_len optional int32 [B] on the device. Returns o.
 
     Paged cache: block_table int32 [B, pages_per_seq] on the device, k / v page pools
-    [pages, page_size, Hkv, d]; max_kv_len defaults to pages_per_seq * page_size."""
+    [pages, page_size, Hkv, d]; max_kv_len defaults to pages_per_seq * page_size.
+    window: sliding window in keys (the query sees the last window keys; 0 = none)."""
     import torch
 
     dev = q.device
@@ -404,7 +411,7 @@ def blasst_attn_decode(q, k, v, *, kv_len=None, lam: float = 0.0, softmax_scale:
     a = _decode_args(q, k, v, o, kv_len=kv_len, lam=lam, softmax_scale=softmax_scale, lse=lse,
                      counters=counters, tile_status=tile_status, tile_margin=tile_margin,
                      block_r=block_r, block_c=block_c, num_splits=num_splits,
-                     block_table=block_table, max_kv_len=max_kv_len)
+                     block_table=block_table, max_kv_len=max_kv_len, window=window)
     lib = load_library()
     need = int(lib.blasst_decode_workspace_size(ctypes.byref(a)))
     if need and workspace is None:

@@ -185,6 +185,8 @@ blasst_status blasst_attn_prefill(const blasst_prefill_args *a, void *stream) {
     return BLASST_ERR_INVALID_ARG;
   if (a->heads_q % a->heads_kv != 0) return BLASST_ERR_INVALID_ARG;
   if (a->causal && a->len_q != a->len_kv) return BLASST_ERR_INVALID_ARG;
+  if (a->window < 0) return BLASST_ERR_INVALID_ARG;
+  if (a->window > 0 && !a->causal) return BLASST_ERR_UNSUPPORTED;
   if (!finite_nonneg(a->lambda)) return BLASST_ERR_INVALID_ARG;
   if (!(a->softmax_scale >= 0.f) || !isfinite(a->softmax_scale)) return BLASST_ERR_INVALID_ARG;
   if (a->head_dim != 64 && a->head_dim != 128) return BLASST_ERR_UNSUPPORTED;
@@ -219,6 +221,7 @@ blasst_status blasst_attn_prefill(const blasst_prefill_args *a, void *stream) {
   p.counters = a->counters;
   p.tile_status = a->tile_status;
   p.tile_margin = a->tile_margin;
+  p.window = a->window;
   const hipError_t err =
       blasst::launch_prefill(p, a->dtype == BLASST_BF16 ? 1 : 0, a->head_dim, br,
                              (hipStream_t)stream);
@@ -253,13 +256,22 @@ int auto_splits(int units, int n_tiles) {
   return s < 1 ? 1 : s;
 }
 
+// Tiles the splits of one sequence divide: all of max_kv_len, or with a sliding window the at
+// most ceil(window / B_c) + 1 tiles a window of that many keys can touch.
+int split_span(const blasst_decode_args *a, int bc) {
+  const int n_tiles = ceil_div(a->max_kv_len, bc);
+  if (a->window <= 0) return n_tiles;
+  const int w = ceil_div(a->window, bc) + 1;
+  return w < n_tiles ? w : n_tiles;
+}
+
 }  // namespace
 
 blasst_status blasst_decode_plan(const blasst_decode_args *a, int32_t *block_r, int32_t *block_c,
                                  int32_t *num_splits) {
   if (!a || !block_r || !block_c || !num_splits) return BLASST_ERR_INVALID_ARG;
   if (a->heads_q <= 0 || a->heads_kv <= 0 || a->heads_q % a->heads_kv != 0 || a->batch < 0 ||
-      a->max_kv_len < 0)
+      a->max_kv_len < 0 || a->window < 0)
     return BLASST_ERR_INVALID_ARG;
   const DecodeKind kind = decode_kind(a);
   if (kind == kNone) return BLASST_ERR_UNSUPPORTED;
@@ -275,12 +287,11 @@ blasst_status blasst_decode_plan(const blasst_decode_args *a, int32_t *block_r, 
     if (br != 64) return BLASST_ERR_UNSUPPORTED;
   }
   if (br > group) br = group;
-  const int n_tiles = ceil_div(a->max_kv_len, bc);
   int s = a->num_splits;
   if (s < 0) return BLASST_ERR_INVALID_ARG;
   if (s == 0) {
     const int units = a->batch * a->heads_kv * ceil_div(group, br);
-    s = auto_splits(units > 0 ? units : 1, n_tiles);
+    s = auto_splits(units > 0 ? units : 1, split_span(a, bc));
   }
   if (s > 256) return BLASST_ERR_UNSUPPORTED;
   *block_r = br;
@@ -341,7 +352,9 @@ blasst_status blasst_attn_decode(const blasst_decode_args *a, void *workspace,
   p.n_rblocks = ceil_div(p.group, br);
   p.n_tiles = ceil_div(a->max_kv_len, bc);
   p.num_splits = s;
-  p.tiles_per_split = p.n_tiles > 0 ? ceil_div(p.n_tiles, s) : 0;
+  const int span = split_span(a, bc);
+  p.tiles_per_split = span > 0 ? ceil_div(span, s) : 0;
+  p.window = a->window;
   p.scale_log2 = scale_log2(a->softmax_scale, a->head_dim_qk);
   p.tau_log2 = tau_log2(a->lambda);
   p.lse = a->lse;

@@ -75,7 +75,11 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
   int seq_len = p.kv_len ? p.kv_len[b] : p.max_kv_len;
   seq_len = max(0, min(seq_len, p.max_kv_len));
   const int seq_tiles = (seq_len + kBlockC - 1) / kBlockC;
-  const int t_begin = split * p.tiles_per_split;
+  // Sliding window: the query sees keys from seq_len - window on; the splits cut the tiles from
+  // the one holding that key.
+  const int first_key = p.window > 0 ? max(0, seq_len - p.window) : 0;
+  const int t_base = first_key / kBlockC;
+  const int t_begin = t_base + split * p.tiles_per_split;
   const int t_split_end = min(t_begin + p.tiles_per_split, p.n_tiles);
   const int t_end = min(t_split_end, seq_tiles);
 
@@ -168,12 +172,14 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
           sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[kb * STEPS + s], qf[s], sacc[kb],
                                                               0, 0, 0);
       }
-      if ((t + 1) * kBlockC > seq_len) {
+      if ((t + 1) * kBlockC > seq_len || t * kBlockC < first_key) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (t * kBlockC + 16 * kb + 4 * kgrp + i >= seq_len) sacc[kb][i] = -INFINITY;
+          for (int i = 0; i < 4; ++i) {
+            const int key = t * kBlockC + 16 * kb + 4 * kgrp + i;
+            if (key >= seq_len || key < first_key) sacc[kb][i] = -INFINITY;
+          }
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -326,7 +332,14 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
     atomicAdd(&p.counters[1], (unsigned long long)skipped);
   }
   if (tid == 0 && (p.tile_status || p.tile_margin)) {
-    for (int t = max(t_begin, t_end); t < t_split_end; ++t) {
+    // Not visited: the rest of this split's range past the sequence; with a window, split 0
+    // also marks the tiles before it and the last split those after every split's range.
+    const int cover_end = min(t_base + p.num_splits * p.tiles_per_split, p.n_tiles);
+    for (int t = 0; t < p.n_tiles; ++t) {
+      const bool mine = (t >= max(t_begin, t_end) && t < t_split_end) ||
+                        (split == 0 && t < t_base) ||
+                        (split == p.num_splits - 1 && t >= cover_end);
+      if (!mine) continue;
       if (p.tile_status) p.tile_status[unit_tiles + t] = 2;
       if (p.tile_margin) p.tile_margin[unit_tiles + t] = -INFINITY;
     }

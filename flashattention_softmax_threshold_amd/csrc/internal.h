@@ -26,6 +26,7 @@ struct PrefillParams {
   unsigned long long *counters;
   uint8_t *tile_status;
   float *tile_margin;
+  int window;  // causal sliding window in keys (row i sees keys i - window + 1 .. i); 0 = none
 };
 
 // dtype: 0 fp32, 1 bf16. Returns hipSuccess or the launch error.
@@ -63,6 +64,9 @@ struct DecodeParams {
   const int32_t *block_table;
   int page_shift;
   int pages_per_seq;
+  // sliding window (> 0): sequence b sees keys max(0, kv_len - window) ..; split s of it covers
+  // tiles first_tile + s * tiles_per_split .. (first_tile = that key / B_c). 0 = none.
+  int window;
 };
 
 hipError_t launch_decode_gqa(const DecodeParams &p, int head_dim, hipStream_t stream);

@@ -113,7 +113,11 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   int seq_len = p.kv_len ? p.kv_len[b] : p.max_kv_len;
   seq_len = max(0, min(seq_len, p.max_kv_len));
   const int seq_tiles = (seq_len + kBlockC - 1) / kBlockC;
-  const int t_begin = split * p.tiles_per_split;
+  // Sliding window: the query sees keys from seq_len - window on; the splits cut the tiles from
+  // the one holding that key.
+  const int first_key = p.window > 0 ? max(0, seq_len - p.window) : 0;
+  const int t_base = first_key / kBlockC;
+  const int t_begin = t_base + split * p.tiles_per_split;
   const int t_split_end = min(t_begin + p.tiles_per_split, p.n_tiles);
   const int t_end = min(t_split_end, seq_tiles);
   const int n_tiles = max(0, t_end - t_begin);
@@ -225,12 +229,15 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   };
 
   // Score (key) of accumulator element i: 32 kh + 8 (i / 4) + 4 hh + i % 4 within the tile.
+  // Keys past the end and (window) keys before the first visible one score -inf.
   auto mask_tile = [&](int tile, f32x16_t &sacc) {
     const int k0 = tile * kBlockC + 32 * kh;
-    if (k0 + 32 > seq_len) {
+    if (k0 + 32 > seq_len || k0 < first_key) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (k0 + 8 * (i >> 2) + 4 * hh + (i & 3) >= seq_len) sacc[i] = -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (key >= seq_len || key < first_key) sacc[i] = -INFINITY;
+      }
     }
   };
 
@@ -413,7 +420,14 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
       atomicAdd(&p.counters[1], (unsigned long long)skipped);
     }
     if (p.tile_status || p.tile_margin) {
-      for (int t = t_begin + n_tiles; t < t_split_end; ++t) {
+      // Not visited: the rest of this split's range past the sequence; with a window, split 0
+      // also marks the tiles before it and the last split those after every split's range.
+      const int cover_end = min(t_base + p.num_splits * p.tiles_per_split, p.n_tiles);
+      for (int t = 0; t < p.n_tiles; ++t) {
+        const bool mine = (t >= t_begin + n_tiles && t < t_split_end) ||
+                          (split == 0 && t < t_base) ||
+                          (split == p.num_splits - 1 && t >= cover_end);
+        if (!mine) continue;
         if (p.tile_status) p.tile_status[unit_tiles * p.n_tiles + t] = 2;
         if (p.tile_margin) p.tile_margin[unit_tiles * p.n_tiles + t] = -INFINITY;
       }

@@ -91,6 +91,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
 
   int n_tiles = p.n_kvtiles;
   if (p.causal) n_tiles = (min(blk_row0 + BR, p.Lq) - 1) / kBlockC + 1;
+  // Sliding window: tiles before the first row's window are not visited.
+  const int j0 = p.window > 0 ? max(0, blk_row0 - p.window + 1) / kBlockC : 0;
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers for the whole pass.
   constexpr int QF = BF16 ? D / 16 : D / 2;
@@ -194,11 +196,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   const int64_t unit_tiles =
       (((int64_t)b * p.Hq + hq) * p.n_qblocks + qb) * (int64_t)p.n_kvtiles;
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(j0);
+  store_tile(j0 & 1);
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
+  for (int j = j0; j < n_tiles; ++j) {
     const int buf = j & 1;
     const int k0 = j * kBlockC;
     if (j + 1 < n_tiles) load_tile(j + 1);
@@ -228,15 +230,19 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
       }
     }
 
-    // ---- Mask: keys past the end, and (causal) keys after the row's position.
-    const bool need_mask = (k0 + kBlockC > p.Lkv) || (p.causal && k0 + kBlockC - 1 > blk_row0);
+    // ---- Mask: keys past the end, (causal) keys after the row's position and (window) keys
+    // before the row's window.
+    const bool need_mask = (k0 + kBlockC > p.Lkv) || (p.causal && k0 + kBlockC - 1 > blk_row0) ||
+                           (p.window > 0 && k0 <= blk_row0 + BR - 1 - p.window);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (key >= p.Lkv || (p.causal && key > my_row)) sacc[kb][i] = -INFINITY;
+          if (key >= p.Lkv || (p.causal && key > my_row) ||
+              (p.window > 0 && key <= my_row - p.window))
+            sacc[kb][i] = -INFINITY;
         }
       }
     }
@@ -379,7 +385,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
       atomicAdd(&p.counters[1], (unsigned long long)skipped);
     }
     if (p.tile_status || p.tile_margin) {
-      for (int j = n_tiles; j < p.n_kvtiles; ++j) {
+      for (int j = 0; j < p.n_kvtiles; ++j) {
+        if (j >= j0 && j < n_tiles) continue;
         if (p.tile_status) p.tile_status[unit_tiles + j] = 2;
         if (p.tile_margin) p.tile_margin[unit_tiles + j] = -INFINITY;
       }

@@ -136,6 +136,9 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
   const bool row_ok = my_row < p.Lq;
   int n_tiles = p.n_kvtiles;
   if (p.causal) n_tiles = (min(blk_row0 + kBR, p.Lq) - 1) / kBlockC + 1;
+  // Sliding window: the block's first row sees keys from blk_row0 - window + 1 on, so earlier
+  // tiles are not visited.
+  const int j0 = p.window > 0 ? max(0, blk_row0 - p.window + 1) / kBlockC : 0;
 
   // ---- Q fragments: B operand of S^T = K Q^T (k = head dim, n = query row).
   bf16x8_t qf[D / 16];
@@ -243,16 +246,20 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
     }
   };
 
-  // Keys past the end and (causal) keys after the row's position score -inf.
+  // Keys past the end, (causal) keys after the row's position and (window) keys before the
+  // row's window score -inf.
   auto mask_tile = [&](int j, f32x16_t *sacc) {
     const int k0 = j * kBlockC;
-    if ((k0 + kBlockC > p.Lkv) || (p.causal && k0 + kBlockC - 1 > blk_row0)) {
+    if ((k0 + kBlockC > p.Lkv) || (p.causal && k0 + kBlockC - 1 > blk_row0) ||
+        (p.window > 0 && k0 <= blk_row0 + kBR - 1 - p.window)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (key >= p.Lkv || (p.causal && key > my_row)) sacc[kb][i] = -INFINITY;
+          if (key >= p.Lkv || (p.causal && key > my_row) ||
+              (p.window > 0 && key <= my_row - p.window))
+            sacc[kb][i] = -INFINITY;
         }
       }
     }
@@ -405,15 +412,15 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
     }
   };
   f32x16_t sa[2], sb[2];
-  issue_k(0, 0);
+  issue_k(j0, j0 & 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (n_tiles > 1) issue_k(1, 1);
-  issue_v(0, 0);
-  compute_s(0, sa);
-  mask_tile(0, sa);
-  publish_margin(0, vote_tile(0, sa));
-  int j = 1;
+  if (n_tiles > j0 + 1) issue_k(j0 + 1, (j0 + 1) & 1);
+  issue_v(j0, j0 & 1);
+  compute_s(j0 & 1, sa);
+  mask_tile(j0, sa);
+  publish_margin(j0, vote_tile(j0, sa));
+  int j = j0 + 1;
   for (; j + 1 < n_tiles; j += 2) {
     step(j, sb, sa);
     step(j + 1, sa, sb);
@@ -451,7 +458,8 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
       atomicAdd(&p.counters[1], (unsigned long long)skipped);
     }
     if (p.tile_status || p.tile_margin) {
-      for (int j = n_tiles; j < p.n_kvtiles; ++j) {
+      for (int j = 0; j < p.n_kvtiles; ++j) {
+        if (j >= j0 && j < n_tiles) continue;
         if (p.tile_status) p.tile_status[unit_tiles + j] = 2;
         if (p.tile_margin) p.tile_margin[unit_tiles + j] = -INFINITY;
       }

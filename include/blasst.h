@@ -151,6 +151,11 @@ typedef enum blasst_dtype { BLASST_F32 = 0, BLASST_BF16 = 1 } blasst_dtype;
  * of the block can see is not visited. The skip test is taken per (unit, tile) over all block_r
  * rows; a row that sees no key of the tile votes "skip".
  *
+ * Sliding window (window > 0, causal only; the BLASST talk notes' Q&A names windowed attention
+ * as structured sparsity the method carries over to): query position i sees keys
+ * max(0, i - window + 1) .. i. Key tiles before every row of a block's window are not visited,
+ * and keys outside a row's window score -inf. window 0 = no window.
+ *
  * Supported: dtype BLASST_BF16 or BLASST_F32, head_dim 64 or 128, block_r 32, 64 or 128
  * (default 128 for bf16, 64 for fp32), block_c 64 (blasst_prefill_tiles resolves defaults). softmax_scale 0 means 1/sqrt(head_dim). o is written in dtype; lse in natural
  * log units. Observation outputs: tile_status / tile_margin are
@@ -170,6 +175,7 @@ typedef struct blasst_prefill_args {
   uint8_t *tile_status;
   float *tile_margin;
   int32_t block_r, block_c; /* 0 = default */
+  int32_t window;           /* sliding window in keys (causal only); 0 = none */
 } blasst_prefill_args;
 
 blasst_status blasst_attn_prefill(const blasst_prefill_args *args, void *stream);
@@ -196,6 +202,11 @@ blasst_status blasst_prefill_tiles(const blasst_prefill_args *args, int32_t *blo
  * are cut into S runs of ceil(ceil(max_kv_len / block_c) / S) tiles; each run restarts the
  * running max, writes a partial (o, lse) to the workspace and a merge kernel combines them by
  * log-sum-exp. num_splits 0 = chosen by the library (blasst_decode_plan reports the choice).
+ *
+ * Sliding window (window > 0): the query of sequence b (at position kv_len[b] - 1) sees keys
+ * max(0, kv_len[b] - window) .. kv_len[b] - 1. The splits then cut the at most
+ * ceil(window / block_c) + 1 tiles a window touches, starting at the tile that holds the
+ * sequence's first visible key; tiles outside every split are not visited. window 0 = none.
  *
  * Value loads are issued only for kept tiles. With v == k and head_dim_v < head_dim_qk (MLA
  * shape) the value tile is read from the key tile already on chip, so skipping saves compute.
@@ -232,6 +243,7 @@ typedef struct blasst_decode_args {
   int32_t block_r, block_c, num_splits; /* 0 = default / automatic */
   const int32_t *block_table;           /* optional paged cache: device [batch, pages_per_seq] */
   int32_t page_size, pages_per_seq;
+  int32_t window;                       /* sliding window in keys; 0 = none */
 } blasst_decode_args;
 
 /* Resolved launch plan of a decode call: tile shape and split count. */

@@ -166,6 +166,8 @@ def _prefill_struct(**over):
     (dict(o=(1 << 20) + 8), F.BLASST_ERR_INVALID_ARG),
     (dict(len_kv=0), F.BLASST_ERR_INVALID_ARG),
     (dict(dtype=5), F.BLASST_ERR_UNSUPPORTED),
+    (dict(causal=1, window=-1), F.BLASST_ERR_INVALID_ARG),
+    (dict(causal=0, window=16), F.BLASST_ERR_UNSUPPORTED),  # windows are causal only
 ])
 def test_prefill_rejects_bad_arguments_before_launch(over, code):
     a = _prefill_struct(**over)
@@ -215,6 +217,21 @@ def test_decode_rejects_bad_arguments_before_launch():
         a.page_size, a.pages_per_seq = page_size, pages
         assert lib.blasst_attn_decode(ctypes.byref(a), None, 0, None) == F.BLASST_ERR_INVALID_ARG, \
             (page_size, pages)
+    a.block_table, a.page_size, a.pages_per_seq = None, 0, 0
+    a.window = -5
+    assert lib.blasst_attn_decode(ctypes.byref(a), None, 0, None) == F.BLASST_ERR_INVALID_ARG
+
+
+def test_decode_plan_with_window_splits_the_window_span():
+    # MLA shape, 32 sequences x 2 row blocks = 64 units: without a window the 1024 tiles of 64K
+    # keys get 8 splits of 128 tiles; a 4096-key window touches at most 65 tiles, cut 8 ways
+    # (ceil(65 / 8) = 9 tiles per split), and a short window with few tiles is not split.
+    q, k = _meta((32, 128, 576)), _meta((32, 65536, 1, 576))
+    v = k[..., :512]
+    assert F.blasst_decode_plan(q, k, v) == (64, 64, 8)
+    assert F.blasst_decode_plan(q, k, v, window=4096) == (64, 64, 8)
+    assert F.blasst_decode_plan(q, k, v, window=300) == (64, 64, 1)
+    assert F.blasst_decode_workspace_size(q, k, v, window=300) == 0
 
 
 # ------------------------------------------------------------------------------------------

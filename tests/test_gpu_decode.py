@@ -16,10 +16,11 @@ pytestmark = pytest.mark.gpu
 
 
 def _run_gpu(q, k, v, kv_len, *, lam, num_splits=0, block_r=0, block_table=None,
-             max_kv_len=None):
+             max_kv_len=None, window=0):
     B, Hq, Dqk = q.shape
     br, bc, S = F.blasst_decode_plan(q, k, v, block_r=block_r, num_splits=num_splits,
-                                     block_table=block_table, max_kv_len=max_kv_len)
+                                     block_table=block_table, max_kv_len=max_kv_len,
+                                     window=window)
     Hkv = k.shape[2]
     n_rb = -(-(Hq // Hkv) // br)
     nt = -(-(k.shape[1] if max_kv_len is None else max_kv_len) // bc)
@@ -30,13 +31,13 @@ def _run_gpu(q, k, v, kv_len, *, lam, num_splits=0, block_r=0, block_table=None,
     o = F.blasst_attn_decode(q, k, v, kv_len=kv_len, lam=lam, lse=lse, counters=cnt,
                              tile_status=ts, tile_margin=tm, block_r=block_r,
                              num_splits=num_splits, block_table=block_table,
-                             max_kv_len=max_kv_len)
+                             max_kv_len=max_kv_len, window=window)
     torch.cuda.synchronize()
     return dict(o=o, lse=lse, status=ts.cpu().numpy(), margin=tm.cpu().numpy(),
                 counters=cnt.cpu().tolist(), br=br, bc=bc, splits=S)
 
 
-def _check(res, ref, q, k, v, lam, what, kv_len):
+def _check(res, ref, q, k, v, lam, what, kv_len, window=0):
     """Decisions agree outside the margin band; a unit with in-band flips is compared against
     the oracle evaluated with the GPU's decisions."""
     o_gpu = res["o"].float().cpu().numpy().astype(np.float64)
@@ -62,7 +63,7 @@ def _check(res, ref, q, k, v, lam, what, kv_len):
     if flipped:
         forced = oracle.decode(q, k, v, kv_len=kv_len, block_r=br, block_c=res["bc"],
                                num_splits=res["splits"], scale=oracle_scale(q.shape[2]), lam=lam,
-                               units=list(flipped), forced=flipped, threads=16)
+                               units=list(flipped), forced=flipped, threads=16, window=window)
         units.update(forced.units)
     og, orf, lg, lr = [], [], [], []
     for (b, g, rb), u in units.items():
@@ -78,7 +79,7 @@ def _check(res, ref, q, k, v, lam, what, kv_len):
 
 
 def _case(B, Hq, Hkv, L, D, kv_len, lams, splits, beta, share, seed, block_r=0, Dv=None,
-          cluster_len=100):
+          cluster_len=100, window=0):
     need_gpu()
     Dv = D if Dv is None else Dv
     mla = Dv != D
@@ -95,13 +96,14 @@ def _case(B, Hq, Hkv, L, D, kv_len, lams, splits, beta, share, seed, block_r=0, 
     skipped = 0
     for S in splits:
         for lam in lams:
-            what = f"decode B{B} H{Hq}/{Hkv} L{L} d{D}/{Dv} S={S} beta={beta} lam={lam}"
+            what = (f"decode B{B} H{Hq}/{Hkv} L{L} d{D}/{Dv} S={S} beta={beta} lam={lam} "
+                    f"window={window}")
             print(what, flush=True)
-            res = _run_gpu(qd, kd, vd, kvd, lam=lam, num_splits=S, block_r=block_r)
+            res = _run_gpu(qd, kd, vd, kvd, lam=lam, num_splits=S, block_r=block_r, window=window)
             ref = oracle.decode(q, k, v, kv_len=kvl, block_r=res["br"], block_c=res["bc"],
                                 num_splits=res["splits"], scale=oracle_scale(D), lam=lam,
-                                threads=8)
-            band_mism = _check(res, ref, q, k, v, lam, what, kvl)
+                                threads=8, window=window)
+            band_mism = _check(res, ref, q, k, v, lam, what, kvl, window)
             assert res["counters"][0] == ref.visited
             assert abs(res["counters"][1] - ref.skipped) <= band_mism
             skipped += ref.skipped
@@ -159,6 +161,29 @@ def test_mla_small_lengths_and_splits():
                  cluster_len=128) > 0
 
 
+def test_gqa_sliding_window_lengths_and_splits():
+    """Sliding windows of one key, shorter than a tile, and a few tiles not a multiple of the
+    tile, on ragged lengths (one sequence shorter than the window), unsplit and split."""
+    L = 1300
+    kv_len = [1300, 1, 200, 1029]
+    for w, seed in ((1, 41), (50, 42), (333, 43)):
+        n = _case(4, 8, 2, L, 128, kv_len, [0.0, 16 / w, 1.0], (1, 2, 0), 16.0, False, seed=seed,
+                  window=w)
+        assert n > 0 or w == 1
+
+
+def test_mla_sliding_window_and_splits():
+    L = 900
+    assert _case(2, 128, 1, L, 576, [900, 300], [0.0, 16 / 400, 1.0], (1, 3), 16.0, True,
+                 seed=44, Dv=512, cluster_len=128, window=400) > 0
+
+
+def test_paged_gqa_sliding_window_equals_contiguous_bitwise():
+    _paged_vs_contiguous(B=2, Hq=8, Hkv=2, L=1000, D=128, Dv=128, kv_len=[1000, 450],
+                         page_sizes=(16, 128), lams=(0.0, 16 / 300), splits=(1, 2), beta=16.0,
+                         share=True, seed=8400, window=300)
+
+
 def test_mla_decode_full_size_sampled():
     """MLA-shaped decode at full size: 32 sequences x 128 heads, KV 65536, d_qk 576 / d_v 512."""
     need_gpu()
@@ -187,7 +212,7 @@ def test_mla_decode_full_size_sampled():
 # output must equal the contiguous call on the same keys bit for bit.
 # ------------------------------------------------------------------------------------------
 def _paged_vs_contiguous(B, Hq, Hkv, L, D, Dv, kv_len, page_sizes, lams, splits, beta, share, seed,
-                         cluster_len=100):
+                         cluster_len=100, window=0):
     need_gpu()
     mla = Dv != D
     q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=Hkv, L=L, d_qk=D, d_v=Dv, cluster_len=cluster_len,
@@ -199,9 +224,9 @@ def _paged_vs_contiguous(B, Hq, Hkv, L, D, Dv, kv_len, page_sizes, lams, splits,
             for lam in lams:
                 what = f"paged decode B{B} H{Hq}/{Hkv} L{L} d{D}/{Dv} page {ps} S={S} lam={lam}"
                 print(what, flush=True)
-                ref = _run_gpu(q, k, v, kvl, lam=lam, num_splits=S)
+                ref = _run_gpu(q, k, v, kvl, lam=lam, num_splits=S, window=window)
                 got = _run_gpu(q, kp, vp, kvl, lam=lam, num_splits=S, block_table=table,
-                               max_kv_len=L)
+                               max_kv_len=L, window=window)
                 assert got["splits"] == ref["splits"]
                 assert torch.equal(got["o"], ref["o"]), what
                 assert np.array_equal(got["lse"].cpu().numpy(), ref["lse"].cpu().numpy()), what

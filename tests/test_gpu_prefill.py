@@ -16,7 +16,7 @@ from parity import (MARGIN_BAND, assert_lse_close, assert_outputs_close, compare
 pytestmark = pytest.mark.gpu
 
 
-def _run_gpu(q, k, v, *, causal, lam, block_r=0):
+def _run_gpu(q, k, v, *, causal, lam, block_r=0, window=0):
     B, Lq, Hq, D = q.shape
     br, bc = F.blasst_prefill_tiles(q, k, block_r=block_r)
     nqb, nkt = -(-Lq // br), -(-k.shape[1] // bc)
@@ -25,13 +25,13 @@ def _run_gpu(q, k, v, *, causal, lam, block_r=0):
     lse = torch.zeros((B, Hq, Lq), dtype=torch.float32, device=q.device)
     cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
     o = F.blasst_attn_prefill(q, k, v, causal=causal, lam=lam, lse=lse, counters=cnt,
-                              tile_status=ts, tile_margin=tm, block_r=block_r)
+                              tile_status=ts, tile_margin=tm, block_r=block_r, window=window)
     torch.cuda.synchronize()
     return dict(o=o, lse=lse, status=ts.cpu().numpy(), margin=tm.cpu().numpy(),
                 counters=cnt.cpu().tolist(), br=br, bc=bc)
 
 
-def _check_units(res, ref, q, k, v, causal, lam, what):
+def _check_units(res, ref, q, k, v, causal, lam, what, window=0):
     """Compare the oracle's units with the GPU outputs of the same units.
 
     Tile decisions must agree outside the margin band. A unit whose decisions differ inside the
@@ -57,7 +57,7 @@ def _check_units(res, ref, q, k, v, causal, lam, what):
     if flipped:
         forced = oracle.prefill(q, k, v, causal=causal, block_r=br, block_c=res["bc"],
                                 scale=oracle_scale(q.shape[3]), lam=lam, units=list(flipped),
-                                forced=flipped, threads=16)
+                                forced=flipped, threads=16, window=window)
         units.update(forced.units)
     og, orf, lg, lr = [], [], [], []
     for (b, h, qb), u in units.items():
@@ -73,19 +73,21 @@ def _check_units(res, ref, q, k, v, causal, lam, what):
     return err, band_mism, band
 
 
-def _case(B, L, Hq, Hkv, D, dtype, causal, block_r, beta, lams, seed, cluster_len=64, sinks=0):
+def _case(B, L, Hq, Hkv, D, dtype, causal, block_r, beta, lams, seed, cluster_len=64, sinks=0,
+          window=0):
     need_gpu()
     q, k, v = prefill_inputs(B=B, L=L, Hq=Hq, Hkv=Hkv, d=D, cluster_len=cluster_len, dtype=dtype,
                              seed=seed, beta=beta, sinks=sinks)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     skipped_any = False
     for lam in lams:
-        what = f"prefill B{B} L{L} H{Hq}/{Hkv} d{D} {dtype} causal={causal} br={block_r} beta={beta} lam={lam}"
+        what = (f"prefill B{B} L{L} H{Hq}/{Hkv} d{D} {dtype} causal={causal} br={block_r} "
+                f"beta={beta} lam={lam} window={window}")
         print(what, flush=True)
-        res = _run_gpu(qd, kd, vd, causal=causal, lam=lam, block_r=block_r)
+        res = _run_gpu(qd, kd, vd, causal=causal, lam=lam, block_r=block_r, window=window)
         ref = oracle.prefill(q, k, v, causal=causal, block_r=res["br"], block_c=res["bc"],
-                             scale=oracle_scale(D), lam=lam, threads=8)
-        _, band_mism, _ = _check_units(res, ref, q, k, v, causal, lam, what)
+                             scale=oracle_scale(D), lam=lam, threads=8, window=window)
+        _, band_mism, _ = _check_units(res, ref, q, k, v, causal, lam, what, window)
         # Counters: the oracle's totals, up to decisions inside the margin band.
         assert res["counters"][0] == ref.visited
         assert abs(res["counters"][1] - ref.skipped) <= band_mism
@@ -121,11 +123,12 @@ def test_edge_lengths():
     _case(1, 129, 4, 2, 128, torch.float32, False, 32, 8.0, [0.0, 1.0], seed=13)
 
 
-def _sampled_full_size(q, k, v, causal, lam, units, what):
-    res = _run_gpu(q, k, v, causal=causal, lam=lam)
+def _sampled_full_size(q, k, v, causal, lam, units, what, window=0):
+    res = _run_gpu(q, k, v, causal=causal, lam=lam, window=window)
     ref = oracle.prefill(q, k, v, causal=causal, block_r=res["br"], block_c=res["bc"],
-                         scale=oracle_scale(q.shape[3]), lam=lam, units=units, threads=16)
-    err, band_mism, band = _check_units(res, ref, q, k, v, causal, lam, what)
+                         scale=oracle_scale(q.shape[3]), lam=lam, units=units, threads=16,
+                         window=window)
+    err, band_mism, band = _check_units(res, ref, q, k, v, causal, lam, what, window)
     # Whole-call counters agree with the whole-call tile map the kernel wrote.
     st = res["status"]
     assert res["counters"][0] == int((st != 2).sum())
@@ -149,6 +152,37 @@ def test_causal_gqa_8k_full_size_sampled(beta):
         res, ref = _sampled_full_size(q, k, v, True, a / L, units, what)
         if beta > 1:
             assert ref.skipped > 0
+
+
+@pytest.mark.parametrize("block_r", [128, 64])
+def test_bf16_causal_gqa_sliding_window(block_r):
+    """Causal sliding windows: one key (the diagonal only), shorter than a tile, a few tiles
+    and not a multiple of the tile, on ragged lengths. (Windows shorter than a tile leave every
+    visited tile holding some row's own maximum, so only the longest one skips.)"""
+    L = 1000
+    for w, seed in ((1, 20), (40, 21), (333, 22)):
+        skipped = _case(2, L, 8, 2, 128, torch.bfloat16, True, block_r, 32.0, [0.0, 16 / w, 1.0],
+                        seed=seed, cluster_len=128, sinks=16, window=w)
+        assert skipped or w < 64
+
+
+def test_fp32_causal_sliding_window():
+    assert _case(1, 400, 2, 1, 64, torch.float32, True, 64, 16.0, [0.0, 0.5], seed=23,
+                 cluster_len=32, window=250)
+
+
+def test_causal_gqa_8k_sliding_window_full_size_sampled():
+    """The full-size causal GQA workload with a 2048-key window."""
+    need_gpu()
+    L, W = 8192, 2048
+    q, k, v = prefill_inputs(B=1, L=L, Hq=32, Hkv=8, d=128, cluster_len=256,
+                             dtype=torch.bfloat16, device="cuda", seed=2000, beta=32.0, sinks=64)
+    units = [(0, 0, 0), (0, 31, 63), (0, 5, 20), (0, 12, 16), (0, 20, 40)]
+    for a in (16, 64):
+        what = f"C2 window={W} lam={a}/W"
+        print(what, flush=True)
+        res, ref = _sampled_full_size(q, k, v, True, a / W, units, what, window=W)
+        assert ref.skipped > 0
 
 
 @pytest.mark.parametrize("beta", [1.0, 4.0])
