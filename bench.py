@@ -337,8 +337,8 @@ def _decode_part(F, torch, args, dev, stream, out):
     paged = []
     la = 16.0 / D["L"]
     ms_c = next(pt["ms"] for pt in dec if pt["lambda"] == "16/L") if args.a in (None, 16.0) else None
-    for ps in PAGE_SIZES:
-        kp, vp, table = paged_layout(kd, vd, ps, seed=D["seed"] + ps)
+    for ps, hm in [(ps, hm) for hm in (False, True) for ps in PAGE_SIZES]:
+        kp, vp, table = paged_layout(kd, vd, ps, seed=D["seed"] + ps, heads_major=hm)
         fn = lambda: F.blasst_attn_decode(qd, kp, vp, kv_len=kvl, lam=la, o=od,  # noqa: E731
                                           workspace=wsd, block_table=table, max_kv_len=D["L"],
                                           stream=stream)
@@ -349,11 +349,12 @@ def _decode_part(F, torch, args, dev, stream, out):
         torch.cuda.synchronize()
         vis, sk = (int(x) for x in cnt.cpu().tolist())
         nbytes = tile_bytes * (2 * vis - sk) + qd.numel() * 2 + od.numel() * 2
-        paged.append({"page_size": ps, "lambda": "16/L", "ms": msp,
+        paged.append({"page_size": ps, "page_layout": "[head, row, dim]" if hm else "[row, head, dim]",
+                      "lambda": "16/L", "ms": msp,
                       "GB/s": nbytes / (msp * 1e-3) / 1e9,
                       "hbm_frac": nbytes / (msp * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       "time_vs_contiguous": (msp / ms_c) if ms_c else None})
-        _progress(f"decode gqa paged {ps}: {msp:.4f} ms")
+        _progress(f"decode gqa paged {ps} heads_major={hm}: {msp:.4f} ms")
         del kp, vp, table
     out["decode_gqa"] = {"workload": "GQA decode B64 Hq32/Hkv8 KV32768 d128 bf16, "
                                      f"centre gain {DECODE_BETA}, tile {brd}x{bcd}, {sd} splits",

@@ -123,7 +123,8 @@ def decode_inputs(*, B: int, Hq: int, Hkv: int, L: int, d_qk: int, d_v: int, clu
     return q, k, v, kv
 
 
-def paged_layout(k, v, page_size: int, *, seed: int = 0, spare_pages: int = 3, kv_len=None):
+def paged_layout(k, v, page_size: int, *, seed: int = 0, spare_pages: int = 3, kv_len=None,
+                 heads_major: bool = False):
     """Scatter a per-sequence cache into shuffled pages of a shared pool (layout only).
 
     k [B, L, Hkv, d_qk], v [B, L, Hkv, d_v] (v may be a view of k's first d_v columns) ->
@@ -131,7 +132,9 @@ def paged_layout(k, v, page_size: int, *, seed: int = 0, spare_pages: int = 3, k
     k_pool[block_table[b, t // page_size], t % page_size] == k[b, t] for the keys each sequence
     uses (all L, or kv_len[b]); pages are drawn in a random order, with `spare_pages` pool pages
     that no sequence uses, so neighbouring keys of a sequence sit in unrelated pages. When v
-    aliases k's first columns, v_pool is the same view of k_pool.
+    aliases k's first columns, v_pool is the same view of k_pool. heads_major: each page is
+    stored [Hkv, page_size, d] (one head's rows of a page contiguous); the pools are returned as
+    [P, page_size, Hkv, d] views of that storage either way.
     """
     B, L, Hkv, dq = k.shape
     dv = v.shape[3]
@@ -141,9 +144,14 @@ def paged_layout(k, v, page_size: int, *, seed: int = 0, spare_pages: int = 3, k
     perm = torch.randperm(n_pages, generator=g)
     table = perm[: B * pps].view(B, pps).to(torch.int32)
     aliases = v.data_ptr() == k.data_ptr() and v.stride() == k.stride() and dv < dq
-    k_pool = torch.zeros((n_pages, page_size, Hkv, dq), dtype=k.dtype, device=k.device)
-    v_pool = k_pool[..., :dv] if aliases else torch.zeros((n_pages, page_size, Hkv, dv),
-                                                          dtype=v.dtype, device=v.device)
+    def pool(d, dtype, device):
+        if heads_major:
+            return torch.zeros((n_pages, Hkv, page_size, d), dtype=dtype,
+                               device=device).transpose(1, 2)
+        return torch.zeros((n_pages, page_size, Hkv, d), dtype=dtype, device=device)
+
+    k_pool = pool(dq, k.dtype, k.device)
+    v_pool = k_pool[..., :dv] if aliases else pool(dv, v.dtype, v.device)
     if kv_len is None and L % page_size == 0:  # every page full: one scatter per pool
         src = k.reshape(B * pps, page_size, Hkv, dq)
         k_pool[table.view(-1).to(k.device)] = src

@@ -212,14 +212,14 @@ def test_mla_decode_full_size_sampled():
 # output must equal the contiguous call on the same keys bit for bit.
 # ------------------------------------------------------------------------------------------
 def _paged_vs_contiguous(B, Hq, Hkv, L, D, Dv, kv_len, page_sizes, lams, splits, beta, share, seed,
-                         cluster_len=100, window=0):
+                         cluster_len=100, window=0, heads_major=False):
     need_gpu()
     mla = Dv != D
     q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=Hkv, L=L, d_qk=D, d_v=Dv, cluster_len=cluster_len,
                                  dtype=torch.bfloat16, device="cuda", seed=seed, beta=beta,
                                  share=share, v_aliases_k=mla, kv_len=kv_len)
     for ps in page_sizes:
-        kp, vp, table = paged_layout(k, v, ps, seed=seed + ps, kv_len=kvl)
+        kp, vp, table = paged_layout(k, v, ps, seed=seed + ps, kv_len=kvl, heads_major=heads_major)
         for S in splits:
             for lam in lams:
                 what = f"paged decode B{B} H{Hq}/{Hkv} L{L} d{D}/{Dv} page {ps} S={S} lam={lam}"
@@ -240,6 +240,13 @@ def test_paged_gqa_equals_contiguous_bitwise():
     _paged_vs_contiguous(B=3, Hq=16, Hkv=4, L=1100, D=128, Dv=128, kv_len=[1100, 517, 0],
                          page_sizes=(1, 16, 64, 256), lams=(0.0, 16 / 1100), splits=(1, 3),
                          beta=16.0, share=True, seed=8100)
+
+
+def test_paged_gqa_heads_major_pages_equal_contiguous_bitwise():
+    # Pages stored [head, row, dim]: the same pools described by other strides.
+    _paged_vs_contiguous(B=2, Hq=16, Hkv=4, L=900, D=128, Dv=128, kv_len=[900, 300],
+                         page_sizes=(16, 64), lams=(0.0, 16 / 900), splits=(1, 2), beta=16.0,
+                         share=True, seed=8500, heads_major=True)
 
 
 def test_paged_gqa_against_oracle():
