@@ -19,9 +19,10 @@
 //   * the waves publish their partial row maxima through LDS; after one barrier every wave forms
 //     the tile maxima and running maxima of all 64 rows of the unit and takes the test itself,
 //     so all four reach the same decision without exchanging votes;
-//   * kept tiles: P = exp2(S - m_ref) of the wave's key half goes to LDS; after a barrier each
-//     wave holds P for all 64 keys and accumulates O^T (256 x 32) += V^T P^T, V^T read from the
-//     same LDS tile with ds_read_b64_tr_b16.
+//   * P = exp2(S - m_ref) of the wave's key half goes to LDS before that barrier, formed with the
+//     current reference max; for a kept tile each wave then holds P for all 64 keys and
+//     accumulates O^T (256 x 32) += V^T P^T, V^T read from the same LDS tile with
+//     ds_read_b64_tr_b16. (A kept tile that moves the reference max forms P again.)
 // LDS layout: the latent parts of a tile's rows (64 x 1024 bytes) and their rotary parts
 // (64 x 128 bytes) are stored apart, 16-byte chunks XOR-swizzled by the row so that the K and
 // V^T reads are conflict-free. A wave-wide copy then moves either one latent row (1 KB of
@@ -76,10 +77,11 @@ constexpr float kRescaleSlack = 8.f;
 
 // LDS stage layout: the latent parts of the 64 rows (1024 bytes each) at 0, the rotary parts
 // (128 bytes each) at kRopeOff. 16-byte chunk c of latent row r sits at chunk c ^ lat_swz(r),
-// chunk c of rotary row r at c ^ (r & 7). lat_swz maps 8 consecutive rows to 8 distinct even (or
-// odd) chunk offsets, so the S reads (8 rows, one chunk) and the transposed V reads (4 rows, two
-// adjacent chunks) each touch distinct banks; the rotary rows alternate bank halves already.
-__device__ __forceinline__ int lat_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// chunk c of rotary row r at c ^ (r & 7). lat_swz is a bijection of r mod 16 that puts the two
+// low row bits on chunk bits 2-3: 16 consecutive rows reading one chunk (the K reads of S) touch
+// 16 distinct 16-byte bank slots, and so do 4 consecutive rows reading 4 consecutive chunks (the
+// transposed V reads of 32 lanes); the rotary rows alternate bank halves already.
+__device__ __forceinline__ int lat_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 
 constexpr int NW = 4;   // waves per workgroup
@@ -189,6 +191,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   float m_run = -INFINITY;    // running max of this wave's rows (base 2)
   float m_run_o = -INFINITY;  // running max of the other row group's rows (for the vote)
   float m_ref = -INFINITY, l_part = 0.f;
+  float m_ref_o = -INFINITY;  // the other row group's reference max (for the rescale decision)
   unsigned visited = 0, skipped = 0;
 
   // S^T for this wave's 32 heads and its 32 keys (key half kh): A = K rows 32 kh + n of stage st,
@@ -196,25 +199,29 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   // loads (next_tile >= 0) go out one per two k-steps between the MFMAs: each inline-asm load is
   // a scheduling boundary, so the reads and MFMAs between two loads stay in source order, and a
   // wave (alone on its SIMD) never stalls on a full load queue with its matrix core idle.
+  // K reads of S: k-step s of this lane (row r = 32 kh + lane % 32, hb = lane / 32) reads
+  // logical chunk 2 s + hb; for s < 32 that is physical chunk (2 s) ^ g, g = hb ^ lat_swz(r),
+  // i.e. byte 256 (s / 8) + (32 (s % 8) ^ 16 g) of the row: eight per-lane offsets, computed
+  // once; for s >= 32 the rotary chunk (2 (s - 32)) ^ (hb ^ (r & 7)).
+  uint32_t s_off[8];
+  uint32_t rope_off;
+  {
+    const int r = 32 * kh + (lane & 31), hb = lane >> 5;
+    const uint32_t g16 = (uint32_t)((hb ^ lat_swz(r)) << 4);
+#pragma unroll
+    for (int b8 = 0; b8 < 8; ++b8) s_off[b8] = (uint32_t)(r * kLatBytes) + ((32u * b8) ^ g16);
+    rope_off = (uint32_t)(kRopeOff + r * kRopeBytes) | (uint32_t)((hb ^ (r & 7)) << 4);
+  }
   auto compute_s = [&](int st, int next_tile, int next_pages) {
     constexpr int KPF = 2;
     f32x16_t sacc = (f32x16_t)0.f;
-    // The per-lane offsets below do not change between tiles; the empty asm makes them opaque
-    // so the compiler recomputes them (a few VALU ops) instead of keeping them live.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int nn = ln & 31, hb = ln >> 5;
-    const int r = 32 * kh + nn;
-    // k-step s reads logical chunk 2 s + hb of row r: for s < 32 the latent chunk at physical
-    // ((2 s) ^ g) with g = hb ^ lat_swz(r), i.e. byte (lat | 16 g) ^ 32 (s % 8) + 256 (s / 8);
-    // for s >= 32 the rotary chunk (2 (s - 32)) ^ (hb ^ (r & 7)).
-    const uint32_t lat = (uint32_t)(r * kLatBytes) | (uint32_t)((hb ^ lat_swz(r)) << 4);
-    const uint32_t rope = (uint32_t)(kRopeOff + r * kRopeBytes) | (uint32_t)((hb ^ (r & 7)) << 4);
     const char *sm = smem[st];
+    const char *lat[8];
+#pragma unroll
+    for (int b8 = 0; b8 < 8; ++b8) lat[b8] = sm + s_off[b8];
     auto rdk = [&](int s2) {
-      const uint32_t off = s2 < kLatSteps ? ((lat ^ (32u * (s2 & 7))) + 256u * (s2 >> 3))
-                                          : (rope ^ (32u * (s2 - kLatSteps)));
-      return *(const bf16x8_t *)(sm + off);
+      return s2 < kLatSteps ? *(const bf16x8_t *)(lat[s2 & 7] + 256 * (s2 >> 3))
+                            : *(const bf16x8_t *)(sm + (rope_off ^ (32u * (s2 - kLatSteps))));
     };
     bf16x8_t fr[kSteps];
 #pragma unroll
@@ -252,37 +259,44 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     return valid && !(delta < p.tau_log2);
   };
 
-  auto rescale_to = [&](float m_tile) {
-    if (__ballot(m_tile > m_ref + kRescaleSlack) != 0ull) {
-      const float alpha = exp2_fast(m_ref - ((m_tile == -INFINITY) ? 0.f : m_tile));
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < kDvBlocks; ++db) oacc[db] *= alpha;
-      m_ref = m_tile;
-    }
-  };
 
-  // O^T (this wave's 256 columns) += V^T P^T over the tile's 64 keys: k-step s (keys
-  // 16 s .. 16 s + 15) takes the bf16 P operand pf[s] as B and 8 column blocks of V^T
-  // (transpose reads of the row-major tile, stage st) as A, read RA MFMAs ahead.
-  // pf[0..1]: this wave's own P (keys 32 kh .. + 31), pf[2..3]: its partner's (keys
-  // 32 (kh ^ 1) ..); the sum over keys does not depend on their order, so only the V rows read
-  // for a step follow kh (a wave-uniform address term, no operand selection).
+  // O^T (this wave's 256 columns) += V^T P^T over the tile's 64 keys: k-step ks (keys
+  // 16 ks .. 16 ks + 15) takes as B the bf16 P fragment of those keys -- this wave's own (pf[0..1],
+  // keys 32 kh ..) or its partner's (pf[2..3]) -- and as A 8 column blocks of V^T (transpose
+  // reads of the row-major tile, stage st), read RA MFMAs ahead. The read of column block db,
+  // rows 16 ks + vrow (and + 8) is at a per-lane offset plus 16384 ks: with f = lat_swz(vrow),
+  // chunk 32 kh + 4 db + vcb sits at 32 kh + ((4 db + vcb) ^ f), and the row + 8 at f ^ 2.
+  uint32_t v_off[kDvBlocks], v_off_hi[kDvBlocks];
+  {
+    const int vrow = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int vcb = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int f = lat_swz(vrow);
+#pragma unroll
+    for (int db = 0; db < kDvBlocks; ++db) {
+      const uint32_t base = (uint32_t)(vrow * kLatBytes + 8 * (lane & 1) + 32 * 16 * kh);
+      v_off[db] = base + 16u * (uint32_t)((4 * db + vcb) ^ f);
+      v_off_hi[db] = base + 8u * kLatBytes + 16u * (uint32_t)((4 * db + vcb) ^ f ^ 2);
+    }
+  }
   auto pv = [&](const bf16x8_t *pf, int st) {
-    constexpr int NM = 4 * kDvBlocks;  // 32 MFMAs: (s, db) = (m / 8, m % 8)
+    constexpr int NM = 4 * kDvBlocks;  // 32 MFMAs: (ks, db) = (m / 8, m % 8)
     constexpr int RA = 2;
-    int ln = lane;  // opaque, as in compute_s
-    asm volatile("" : "+v"(ln));
-    const int vrow = 4 * (ln >> 5) + ((ln & 15) >> 2);
-    const int vcb = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
-    const char *vl = smem[st] + 8 * (ln & 1);
+    // B operand of k-step ks: a select of 32-bit words on the wave-uniform kh.
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 own = __builtin_bit_cast(uint4, pf[ks & 1]);
+      const uint4 oth = __builtin_bit_cast(uint4, pf[2 + (ks & 1)]);
+      const bool mine = (ks >> 1) == kh;
+      const uint4 w = make_uint4(mine ? own.x : oth.x, mine ? own.y : oth.y, mine ? own.z : oth.z,
+                                 mine ? own.w : oth.w);
+      pb[ks] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    const char *vl = smem[st];
     auto rdv = [&](int m) {
-      const int s2 = m / kDvBlocks, db = m % kDvBlocks;
-      const int key_step = 2 * (s2 < 2 ? kh : kh ^ 1) + (s2 & 1);  // keys 16 key_step ..
-      const int r0 = 16 * key_step + vrow;
-      const int c = 4 * (kDvBlocks * kh + db) + vcb;  // logical chunk (< 64)
-      const char *p0 = vl + r0 * kLatBytes + 16 * (c ^ lat_swz(r0));
-      const char *p1 = vl + (r0 + 8) * kLatBytes + 16 * (c ^ lat_swz(r0 + 8));
+      const int ks = m / kDvBlocks, db = m % kDvBlocks;
+      const char *p0 = vl + v_off[db] + 16 * kLatBytes * ks;
+      const char *p1 = vl + v_off_hi[db] + 16 * kLatBytes * ks;
       const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
       const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
       return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -294,15 +308,40 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     for (int m = 0; m < NM; ++m) {
       if (m + RA < NM) va[(m + RA) % (RA + 1)] = rdv(m + RA);
       oacc[m % kDvBlocks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m % (RA + 1)],
-                                                                    pf[m / kDvBlocks],
+                                                                    pb[m / kDvBlocks],
                                                                     oacc[m % kDvBlocks], 0, 0, 0);
     }
   };
 
-  // Three barriers per kept tile (two per skipped one): (1) tile j is in LDS, the other stage is
-  // free; (2) every wave's partial row maxima are visible -- each wave then takes the test for
-  // all 64 rows of the unit, so the decision needs no vote exchange; (3) kept tiles only: each
-  // wave's bf16 P for its key half is visible to its partner.
+  // P = 2^(s - m_ref) of this wave's rows and key half in bf16: kept in pf[0..1], published in
+  // sP for the partner; returns the lane's part of the row sums of the rounded P.
+  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+  auto make_p = [&](const f32x16_t &sacc, bf16x8_t *pf) {
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      bf16x8_t pk;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pk[e] = (__bf16)exp2_fast(fmaf(sacc[8 * h2 + e], p.scale_log2, -m_use));
+      const bf16x2_t x0 = {pk[0], pk[1]}, x1 = {pk[2], pk[3]};
+      const bf16x2_t x2 = {pk[4], pk[5]}, x3 = {pk[6], pk[7]};
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(x0, one, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(x1, one, ps1, false);
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(x2, one, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, ps1, false);
+      pf[h2] = pk;
+      sP[wv][h2][lane] = pk;
+    }
+    return ps0 + ps1;
+  };
+
+  // Two barriers per tile: (1) tile j is in LDS, the other stage is free; (2) every wave's
+  // partial row maxima and its bf16 P (formed with the current reference max before the test)
+  // are visible -- each wave then takes the test for all 64 rows of the unit, so the decision
+  // needs no vote exchange. A kept tile that moves the reference max forms P again and
+  // publishes it behind a third barrier.
   // Paged: `ahead` is the table read of the tile after next; it is taken over (as the pages of
   // the next tile's copies) only after the wait at the top of the following step.
   int ahead = 0;
@@ -313,7 +352,6 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     for (int nn = 0; nn < kLoadsPerTile / NW; ++nn) issue_one(t_begin, 0, nn, pages0);
     if (n_tiles > 1) ahead = page_of_lane_key(t_begin + 1);
   }
-  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
   for (int j = 0; j < n_tiles; ++j) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -329,6 +367,11 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
       const float pm = max_halves(max3f(max3f(m[0], m[1], m[2]), max3f(m[3], m[4], m[5]), m[5]));
       if (hh == 0) sPmax[wv][n] = pm;
     }
+    // P of this wave's rows and key half with the current reference max, published before the
+    // test: when the tile is kept and needs no rescale, the partner's half is already visible
+    // after the next barrier.
+    bf16x8_t pf[4];  // own P (keys 32 kh + 16 h2 ..), then the partner's
+    float ps = make_p(sacc, pf);
     __syncthreads();
     float mg_own, mg_oth;
     const bool keep_own =
@@ -349,27 +392,20 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
       if (p.tile_status) p.tile_status[unit_tiles * p.n_tiles + t_begin + j] = keep ? 0 : 1;
     }
     if (keep) {
-      rescale_to(m_run);
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-      bf16x8_t pf[4];  // own P (keys 32 kh + 16 h2 ..), then the partner's
-      float ps0 = 0.f, ps1 = 0.f;
+      // Rescale when some row of the unit has outgrown its reference max by more than the
+      // slack; every wave sees all 64 rows' maxima, so the decision (and the barrier in it) is
+      // the same in every wave. The first kept tile of a split always takes it.
+      if (__ballot(m_run > m_ref + kRescaleSlack || m_run_o > m_ref_o + kRescaleSlack) != 0ull) {
+        const float alpha = exp2_fast(m_ref - ((m_run == -INFINITY) ? 0.f : m_run));
+        l_part *= alpha;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        bf16x8_t pk;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pk[e] = (__bf16)exp2_fast(fmaf(sacc[8 * h2 + e], p.scale_log2, -m_use));
-        const bf16x2_t x0 = {pk[0], pk[1]}, x1 = {pk[2], pk[3]};
-        const bf16x2_t x2 = {pk[4], pk[5]}, x3 = {pk[6], pk[7]};
-        ps0 = __builtin_amdgcn_fdot2_f32_bf16(x0, one, ps0, false);
-        ps1 = __builtin_amdgcn_fdot2_f32_bf16(x1, one, ps1, false);
-        ps0 = __builtin_amdgcn_fdot2_f32_bf16(x2, one, ps0, false);
-        ps1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, ps1, false);
-        pf[h2] = pk;
-        sP[wv][h2][lane] = pk;
+        for (int db = 0; db < kDvBlocks; ++db) oacc[db] *= alpha;
+        m_ref = m_run;
+        m_ref_o = m_run_o;
+        ps = make_p(sacc, pf);
+        __syncthreads();
       }
-      l_part += ps0 + ps1;
-      __syncthreads();
+      l_part += ps;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) pf[2 + h2] = sP[wv ^ 2][h2][lane];
       pv(pf, j & 1);
