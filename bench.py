@@ -156,10 +156,30 @@ def _cpu_baseline(q, k, v, lam, br, bc, budget_s=12.0):
     for (_, _, qb) in done:
         r0, r1 = qb * br, min((qb + 1) * br, L)
         flops += 4.0 * d * sum(r + 1 for r in range(r0, r1))
+    # One thread on a few units, for the per-core rate.
+    one = units[:8]
+    t1 = time.perf_counter()
+    oracle.prefill(qc, kc, vc, causal=True, block_r=br, block_c=bc, scale=1 / math.sqrt(d),
+                   lam=lam, units=one, threads=1)
+    e1 = time.perf_counter() - t1
+    f1 = sum(4.0 * d * sum(r + 1 for r in range(qb * br, min((qb + 1) * br, L)))
+             for (_, _, qb) in one)
     return dict(value=flops / elapsed / 1e12, unit="TFLOP/s (dense-equivalent)", cores=threads,
                 kind="oracle",
                 sample=f"{len(done)} of {len(units)} causal prefill units (random, seed 7), "
-                       f"{elapsed:.1f} s wall, fp64")
+                       f"{elapsed:.1f} s wall, fp64",
+                value_1_thread=f1 / e1 / 1e12, cpu_model=_cpu_model(),
+                host_cpus=os.cpu_count())
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _counter_csv(d):
