@@ -95,8 +95,9 @@ __device__ __forceinline__ int swz_k(int row, int cpr) { return row & (cpr - 1);
 __device__ __forceinline__ int swz_v(int row, int cpr) { return (4 * (row & 3)) & (cpr - 1); }
 
 // NH query heads of one KV group per workgroup (4 waves, i.e. one 128-row unit, per head): the
-// K and V tiles in LDS serve all NH heads, so each wave issues 1 / NH of the loads.
-template <int D, int NH>
+// K and V tiles in LDS serve all NH heads, so each wave issues 1 / NH of the loads. WIN: the
+// call has a sliding window (a separate instance, so calls without one pay nothing for it).
+template <int D, int NH, bool WIN>
 __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillParams p) {
   using G = Geo<D, NH>;
   constexpr int RB = G::ROW_BYTES, CPR = G::CPR;
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
   if (p.causal) n_tiles = (min(blk_row0 + kBR, p.Lq) - 1) / kBlockC + 1;
   // Sliding window: the block's first row sees keys from blk_row0 - window + 1 on, so earlier
   // tiles are not visited.
-  const int j0 = p.window > 0 ? max(0, blk_row0 - p.window + 1) / kBlockC : 0;
+  const int j0 = WIN ? max(0, blk_row0 - p.window + 1) / kBlockC : 0;
 
   // ---- Q fragments: B operand of S^T = K Q^T (k = head dim, n = query row).
   bf16x8_t qf[D / 16];
@@ -251,14 +252,14 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
   auto mask_tile = [&](int j, f32x16_t *sacc) {
     const int k0 = j * kBlockC;
     if ((k0 + kBlockC > p.Lkv) || (p.causal && k0 + kBlockC - 1 > blk_row0) ||
-        (p.window > 0 && k0 <= blk_row0 + kBR - 1 - p.window)) {
+        (WIN && k0 <= blk_row0 + kBR - 1 - p.window)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
           if (key >= p.Lkv || (p.causal && key > my_row) ||
-              (p.window > 0 && key <= my_row - p.window))
+              (WIN && key <= my_row - p.window))
             sacc[kb][i] = -INFINITY;
         }
       }
@@ -472,7 +473,10 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
 template <int D, int NH>
 void launch_nh(const PrefillParams &p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.B * p.Hq / NH * p.n_qblocks));
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, NH>), grid, dim3(kNT * NH), 0, stream, p);
+  if (p.window > 0)
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, true>), grid, dim3(kNT * NH), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, false>), grid, dim3(kNT * NH), 0, stream, p);
 }
 
 // Two heads per workgroup when the query heads of a KV head pair up (even group), else one.
