@@ -49,8 +49,10 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 &u, float *f) {
   }
 }
 
+// Two workgroups per CU (at most 256 registers per wave): twice the K and V loads in flight, which
+// the skip case (V requested only after the vote) and the paged cache (page-number reads) need.
 template <int D, int RB, bool PAGED>
-__global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
   constexpr int STEPS = D / 32;  // k-steps of one 16x16x32 MFMA chain
   constexpr int CPR = D / 8;     // 16-byte chunks per key row
   constexpr int KPI = 64 / CPR;  // keys covered by one V load instruction
