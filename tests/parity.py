@@ -3,7 +3,9 @@
 Bar (bf16 inputs, fp32 accumulation): max|dO| <= 1e-2 * max|O| against the exact oracle and
 mean|dO| <= 1e-3 against the oracle rounded to the output dtype (bf16 rounding of an output of
 magnitude ~1 alone is ~1e-3 on average); LSE within 1e-2 (natural log). fp32 inputs: max|dO| <= 1e-4 * max|O|,
-mean|dO| <= 1e-5, LSE within 1e-4. Skip decisions must agree exactly on every tile whose oracle
+mean|dO| <= 1e-5, LSE within 1e-4 + 2e-6 |LSE|: the LSE is about the largest scaled score, which
+the kernel forms in fp32, so its rounding grows with the score's magnitude (an fp32 ulp at 256 is
+3e-5). Skip decisions must agree exactly on every tile whose oracle
 margin lies outside a band around ln(lambda); inside the band float rounding may flip the
 decision, and such tiles are counted, not failed (their units are then compared against the
 oracle evaluated with the kernel's decisions).
@@ -18,8 +20,8 @@ import torch
 
 MARGIN_BAND = 1e-3
 TOL = {
-    torch.bfloat16: dict(max_rel=1e-2, mean_abs=1e-3, lse_abs=1e-2),
-    torch.float32: dict(max_rel=1e-4, mean_abs=1e-5, lse_abs=1e-4),
+    torch.bfloat16: dict(max_rel=1e-2, mean_abs=1e-3, lse_abs=1e-2, lse_rel=0.0),
+    torch.float32: dict(max_rel=1e-4, mean_abs=1e-5, lse_abs=1e-4, lse_rel=2e-6),
 }
 
 
@@ -51,12 +53,16 @@ def assert_outputs_close(o_gpu: np.ndarray, o_ref: np.ndarray, dtype, what: str)
 
 
 def assert_lse_close(lse_gpu: np.ndarray, lse_ref: np.ndarray, dtype, what: str):
-    tol = TOL[dtype]["lse_abs"]
+    t = TOL[dtype]
     fin = np.isfinite(lse_ref)
     assert np.array_equal(np.isfinite(lse_gpu), fin), f"{what}: LSE finiteness differs"
     if fin.any():
-        d = np.abs(lse_gpu[fin] - lse_ref[fin]).max()
-        assert d <= tol, f"{what}: LSE differs by {d:.3e}"
+        d = np.abs(lse_gpu[fin] - lse_ref[fin])
+        tol = t["lse_abs"] + t["lse_rel"] * np.abs(lse_ref[fin])
+        worst = int(np.argmax(d - tol))
+        assert (d <= tol).all(), \
+            f"{what}: LSE differs by {d[worst]:.3e} (tolerance {tol[worst]:.3e} at |LSE| " \
+            f"{abs(lse_ref[fin][worst]):.3e})"
 
 
 def compare_tile_status(st_gpu: np.ndarray, st_ref: np.ndarray, margin_ref: np.ndarray,
