@@ -298,6 +298,26 @@ def _prefill_part(F, torch, args, dev, stream, out):
                                   "executed_tflops": tile_flops * 2 * v0 / (ms0 * 1e-3) / 1e12}
         out["prefill_sweep"] = sweep
         _progress("prefill sweep done")
+        # Speedup against skip fraction: thresholds at quantiles of the tile margins of one
+        # lambda = 0 call (a tile is skipped exactly when its margin is below ln lambda).
+        from flashattention_softmax_threshold_amd import calibration as C
+        import numpy as np
+
+        margin, status = C.prefill_margins(q, k, v, causal=True)
+        mv = np.sort(margin.cpu().numpy()[status.cpu().numpy() != 2].astype(np.float64))
+        curve = []
+        for f_t in (0.1, 0.3, 0.5, 0.7, 0.9):
+            idx = min(int(f_t * len(mv)), len(mv) - 1)
+            la = min(1.0, math.exp(float(mv[idx])) * (1 + 1e-6))  # just above that margin
+            msa = _time_calls(prefill_step(la), args.steps, args.warmup, stream)
+            va, sa = _prefill_counts(F, q, k, v, la)
+            curve.append({"target_skip": f_t, "lambda": la, "skip_fraction": sa / va, "ms": msa,
+                          "speedup_vs_lambda0": ms0 / msa,
+                          "ceiling_2/(2-f)": 2.0 / (2.0 - sa / va),
+                          "executed_tflops": tile_flops * (2 * va - sa) / (msa * 1e-3) / 1e12})
+        out["prefill_skip_curve"] = curve
+        del margin, status
+        _progress("prefill skip curve done")
         # The recipe read literally (centre gain 1): nothing is skipped; overhead of the test.
         q1, k1, v1 = prefill_inputs(B=P["B"], L=L, Hq=Hq, Hkv=P["Hkv"], d=d,
                                     cluster_len=P["cluster_len"], dtype=torch.bfloat16,
@@ -311,6 +331,14 @@ def _prefill_part(F, torch, args, dev, stream, out):
         del q1, k1, v1
         _progress("prefill centre gain 1 done")
     return q, k, v, lam, br, bc
+
+
+def _literal_gain1(fn_of_lam, lams, steps, warmup, stream):
+    """Times of the same calls on inputs generated at centre gain 1 (the recipe read literally,
+    where nothing is skipped): the cost of taking the test when it never fires."""
+    ms = {f"{k}": _time_calls(fn_of_lam(la), steps, warmup, stream) for k, la in lams}
+    base = ms[lams[0][0]]
+    return {"ms": ms, "time_vs_lambda0": {k: v / base for k, v in ms.items()}}
 
 
 def _sweep_points(args):
@@ -376,9 +404,22 @@ def _decode_part(F, torch, args, dev, stream, out):
                       "time_vs_contiguous": (msp / ms_c) if ms_c else None})
         _progress(f"decode gqa paged {ps} heads_major={hm}: {msp:.4f} ms")
         del kp, vp, table
+    if args.part == "all":
+        del kd, vd
+        q1, k1, v1, kv1 = decode_inputs(B=D["B"], Hq=D["Hq"], Hkv=D["Hkv"], L=D["L"], d_qk=D["d"],
+                                        d_v=D["d"], cluster_len=D["cluster_len"],
+                                        dtype=torch.bfloat16, device=dev, seed=D["seed"],
+                                        beta=1.0)
+        gain1 = _literal_gain1(
+            lambda la: (lambda: F.blasst_attn_decode(q1, k1, v1, kv_len=kv1, lam=la, o=od,
+                                                     workspace=wsd, stream=stream)),
+            [("0", 0.0), ("16/L", 16.0 / D["L"])], args.steps, args.warmup, stream)
+        del q1, k1, v1
+        _progress("decode gqa centre gain 1 done")
     out["decode_gqa"] = {"workload": "GQA decode B64 Hq32/Hkv8 KV32768 d128 bf16, "
                                      f"centre gain {DECODE_BETA}, tile {brd}x{bcd}, {sd} splits",
                          "points": dec, "paged": paged,
+                         "literal_gain1": gain1 if args.part == "all" else None,
                          "traffic_lambda_16/L": _traffic_from_profile(
                              "decode.hip", "decode_gqa_B64_L32768_hbm_counters.json")}
 
@@ -418,9 +459,22 @@ def _mla_part(F, torch, args, dev, stream, out):
                     "executed_tflops": flops / (msm * 1e-3) / 1e12,
                     "speedup_vs_lambda0": (msm0 / msm) if msm0 else None})
         _progress(f"decode mla a={a:g}: {msm:.4f} ms")
+    gain1 = None
+    if args.part == "all":
+        del km, vm
+        q1, k1, v1, kv1 = decode_inputs(B=M["B"], Hq=M["Hq"], Hkv=1, L=M["L"], d_qk=576, d_v=512,
+                                        cluster_len=M["cluster_len"], dtype=torch.bfloat16,
+                                        device=dev, seed=M["seed"], beta=1.0, share=True,
+                                        v_aliases_k=True)
+        gain1 = _literal_gain1(
+            lambda la: (lambda: F.blasst_attn_decode(q1, k1, v1, kv_len=kv1, lam=la, o=om,
+                                                     workspace=wsm, stream=stream)),
+            [("0", 0.0), ("16/L", 16.0 / M["L"])], args.steps, args.warmup, stream)
+        del q1, k1, v1
+        _progress("decode mla centre gain 1 done")
     out["decode_mla"] = {"workload": "MLA-shaped decode B32 Hq128 KV65536 d_qk576/d_v512 bf16, "
                                      f"centre gain {MLA_BETA}, tile {brm}x{bcm}, {sm} splits",
-                         "points": mla,
+                         "points": mla, "literal_gain1": gain1,
                          "traffic_lambda_16/L": _traffic_from_profile(
                              "mla.hip", "decode_mla_B32_L65536_hbm_counters.json")}
 
@@ -457,10 +511,26 @@ def _dit_part(F, torch, args, dev, stream, out):
                     "mfma_frac": ex / BF16_PEAK_TFLOPS, "speedup_vs_lambda0": ms0 / ms,
                     "ceiling_2/(2-f)": 2.0 / (2.0 - sk / vis)})
         _progress(f"video dit s={s_t}: {ms:.3f} ms")
+    del q, k, v
+    q1, k1, v1 = prefill_inputs(B=1, L=L, Hq=H, Hkv=H, d=d, cluster_len=60, dtype=torch.bfloat16,
+                                device=dev, seed=4000, beta=1.0, frame_len=3600, patch_len=60)
+    lam5 = F.blasst_resolve_lambda(F.BLASST_TARGET_SPARSITY, L, target_sparsity=0.5, a=WAN_A,
+                                   b=WAN_B)
+    gain1 = _literal_gain1(
+        lambda la: (lambda: F.blasst_attn_prefill(q1, k1, v1, causal=False, lam=la, o=o,
+                                                  stream=stream)),
+        [("0", 0.0), ("target 0.5", lam5)], steps, warm, stream)
+    cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+    F.blasst_attn_prefill(q1, k1, v1, causal=False, lam=lam5, counters=cnt)
+    torch.cuda.synchronize()
+    vis1, sk1 = (int(x) for x in cnt.cpu().tolist())
+    gain1["skip_fraction_target_0.5"] = sk1 / vis1
+    del q1, k1, v1
+    _progress("video dit centre gain 1 done")
     out["prefill_video_dit"] = {"workload": "non-causal MHA B1 H40 L75600 (21 x 3600) d128 bf16, "
                                             f"tile {br}x{bc}, frame + 60-token patch clusters, "
-                                            f"centre gain {DIT_BETA}", "points": pts}
-    del q, k, v
+                                            f"centre gain {DIT_BETA}", "points": pts,
+                                "literal_gain1": gain1}
 
 
 def _window_part(F, torch, args, dev, stream, out):
