@@ -7,11 +7,11 @@
 // work pays there even though V costs no extra traffic: the V tile is the K tile already on chip.
 //
 // Work unit (one workgroup of 4 waves): (sequence b, block of B_r = 64 heads, split of the key
-// range). Wave w = (row group rg = w % 2, half kh = w / 2) owns query heads 32 rg .. + 31 of the
-// block, the scores of keys 32 kh .. + 31 of each tile, and output columns 256 kh .. + 255: the
-// two waves of a row group form each score once between them (one key half each) and exchange
-// their bf16 P through LDS, so each keeps only half of O (32 rows x 256 columns of fp32) in its
-// accumulation registers. Per key tile of 64 keys:
+// range). For the scores, wave w = (row group rg = w % 2, key half kh = w / 2) takes query heads
+// 32 rg .. + 31 of the block against keys 32 kh .. + 31 of each tile; for P.V, wave w owns output
+// columns 128 w .. + 127 of all 64 heads, so each V^T fragment it reads from LDS feeds two MFMAs
+// (one per row group) and the four waves together read the V part of a tile once per row group
+// pair instead of twice. Per key tile of 64 keys:
 //   * the K tile (64 x 576 bf16, 72 KB) goes from HBM straight into LDS (global_load_lds_dwordx4,
 //     two stages); the next tile's loads are issued between the MFMAs of this tile's scores;
 //   * S^T (32 keys x 32 heads) = K Q^T with v_mfma_f32_32x32x16_bf16 over 36 k-steps: A = K rows
@@ -19,9 +19,9 @@
 //   * the waves publish their partial row maxima through LDS; after one barrier every wave forms
 //     the tile maxima and running maxima of all 64 rows of the unit and takes the test itself,
 //     so all four reach the same decision without exchanging votes;
-//   * P = exp2(S - m_ref) of the wave's key half goes to LDS before that barrier, formed with the
-//     current reference max; for a kept tile each wave then holds P for all 64 keys and
-//     accumulates O^T (256 x 32) += V^T P^T, V^T read from the same LDS tile with
+//   * P = exp2(S - m_ref) of the wave's rows and key half goes to LDS before that barrier, formed
+//     with the current reference max; for a kept tile each wave reads P of all 64 heads and keys
+//     and accumulates O^T (128 x 64) += V^T P^T, V^T read from the same LDS tile with
 //     ds_read_b64_tr_b16. (A kept tile that moves the reference max forms P again.)
 // LDS layout: the latent parts of a tile's rows (64 x 1024 bytes) and their rotary parts
 // (64 x 128 bytes) are stored apart, 16-byte chunks XOR-swizzled by the row so that the K and
@@ -54,7 +54,7 @@ constexpr int kLoadsPerTile = kTileBytes / 1024;    // 72 wave-wide 16-byte load
 constexpr int kRowLoads = kBlockC;                  // 64 of them copy one latent row each
 constexpr int kSteps = kDqk / 16;                   // 36 k-steps of S
 constexpr int kLatSteps = kDv / 16;                 // 32 of them over the latent part
-constexpr int kDvBlocks = kDv / 32 / 2;             // 8 output column blocks per wave
+constexpr int kDvBlocks = kDv / 32 / 4;             // 4 output column blocks per wave
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -185,9 +185,13 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     }
   };
 
-  f32x16_t oacc[kDvBlocks];
+  // O^T of this wave's 128 columns for both row groups of the unit: oacc[rb][db] holds columns
+  // 128 wv + 32 db .. + 31 of heads 32 rb .. + 31.
+  f32x16_t oacc[2][kDvBlocks];
 #pragma unroll
-  for (int db = 0; db < kDvBlocks; ++db) oacc[db] = (f32x16_t)0.f;
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int db = 0; db < kDvBlocks; ++db) oacc[rb][db] = (f32x16_t)0.f;
   float m_run = -INFINITY;    // running max of this wave's rows (base 2)
   float m_run_o = -INFINITY;  // running max of the other row group's rows (for the vote)
   float m_ref = -INFINITY, l_part = 0.f;
@@ -260,12 +264,13 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   };
 
 
-  // O^T (this wave's 256 columns) += V^T P^T over the tile's 64 keys: k-step ks (keys
-  // 16 ks .. 16 ks + 15) takes as B the bf16 P fragment of those keys -- this wave's own (pf[0..1],
-  // keys 32 kh ..) or its partner's (pf[2..3]) -- and as A 8 column blocks of V^T (transpose
-  // reads of the row-major tile, stage st), read RA MFMAs ahead. The read of column block db,
-  // rows 16 ks + vrow (and + 8) is at a per-lane offset plus 16384 ks: with f = lat_swz(vrow),
-  // chunk 32 kh + 4 db + vcb sits at 32 kh + ((4 db + vcb) ^ f), and the row + 8 at f ^ 2.
+  // O^T (this wave's 128 columns, both row groups) += V^T P^T over the tile's 64 keys: k-step ks
+  // (keys 16 ks .. 16 ks + 15) takes as B the bf16 P fragments of those keys for row groups 0 and
+  // 1, as published by waves 2 (ks / 2) and 2 (ks / 2) + 1, and as A 4 column blocks of V^T
+  // (transpose reads of the row-major tile, stage st), each read once, RA reads ahead, for two
+  // MFMAs. The read of column block db, rows 16 ks + vrow (and + 8) is at a per-lane offset plus
+  // 16384 ks: with f = lat_swz(vrow), chunk 16 w + 4 db + vcb sits at 16 w + ((4 db + vcb) ^ f),
+  // and the row + 8 at f ^ 2.
   uint32_t v_off[kDvBlocks], v_off_hi[kDvBlocks];
   {
     const int vrow = 4 * (lane >> 5) + ((lane & 15) >> 2);
@@ -273,25 +278,20 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     const int f = lat_swz(vrow);
 #pragma unroll
     for (int db = 0; db < kDvBlocks; ++db) {
-      const uint32_t base = (uint32_t)(vrow * kLatBytes + 8 * (lane & 1) + 32 * 16 * kh);
+      const uint32_t base = (uint32_t)(vrow * kLatBytes + 8 * (lane & 1) + 16 * 16 * wv);
       v_off[db] = base + 16u * (uint32_t)((4 * db + vcb) ^ f);
       v_off_hi[db] = base + 8u * kLatBytes + 16u * (uint32_t)((4 * db + vcb) ^ f ^ 2);
     }
   }
-  auto pv = [&](const bf16x8_t *pf, int st) {
-    constexpr int NM = 4 * kDvBlocks;  // 32 MFMAs: (ks, db) = (m / 8, m % 8)
+  auto pv = [&](int st) {
+    constexpr int NM = 4 * kDvBlocks;  // 16 V^T fragments: (ks, db) = (m / 4, m % 4)
     constexpr int RA = 2;
-    // B operand of k-step ks: a select of 32-bit words on the wave-uniform kh.
-    bf16x8_t pb[4];
+    // B operands: P of row group rb, k-step ks, as published by wave rb + 2 (ks / 2).
+    bf16x8_t pb[2][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 own = __builtin_bit_cast(uint4, pf[ks & 1]);
-      const uint4 oth = __builtin_bit_cast(uint4, pf[2 + (ks & 1)]);
-      const bool mine = (ks >> 1) == kh;
-      const uint4 w = make_uint4(mine ? own.x : oth.x, mine ? own.y : oth.y, mine ? own.z : oth.z,
-                                 mine ? own.w : oth.w);
-      pb[ks] = __builtin_bit_cast(bf16x8_t, w);
-    }
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) pb[rb][ks] = sP[rb + 2 * (ks >> 1)][ks & 1][lane];
     const char *vl = smem[st];
     auto rdv = [&](int m) {
       const int ks = m / kDvBlocks, db = m % kDvBlocks;
@@ -307,16 +307,17 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       if (m + RA < NM) va[(m + RA) % (RA + 1)] = rdv(m + RA);
-      oacc[m % kDvBlocks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m % (RA + 1)],
-                                                                    pb[m / kDvBlocks],
-                                                                    oacc[m % kDvBlocks], 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        oacc[rb][m % kDvBlocks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            va[m % (RA + 1)], pb[rb][m / kDvBlocks], oacc[rb][m % kDvBlocks], 0, 0, 0);
     }
   };
 
-  // P = 2^(s - m_ref) of this wave's rows and key half in bf16: kept in pf[0..1], published in
-  // sP for the partner; returns the lane's part of the row sums of the rounded P.
+  // P = 2^(s - m_ref) of this wave's rows and key half in bf16, published in sP for every wave's
+  // P.V; returns the lane's part of the row sums of the rounded P.
   const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
-  auto make_p = [&](const f32x16_t &sacc, bf16x8_t *pf) {
+  auto make_p = [&](const f32x16_t &sacc) {
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
@@ -331,7 +332,6 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
       ps1 = __builtin_amdgcn_fdot2_f32_bf16(x1, one, ps1, false);
       ps0 = __builtin_amdgcn_fdot2_f32_bf16(x2, one, ps0, false);
       ps1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, ps1, false);
-      pf[h2] = pk;
       sP[wv][h2][lane] = pk;
     }
     return ps0 + ps1;
@@ -370,8 +370,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     // P of this wave's rows and key half with the current reference max, published before the
     // test: when the tile is kept and needs no rescale, the partner's half is already visible
     // after the next barrier.
-    bf16x8_t pf[4];  // own P (keys 32 kh + 16 h2 ..), then the partner's
-    float ps = make_p(sacc, pf);
+    float ps = make_p(sacc);
     __syncthreads();
     float mg_own, mg_oth;
     const bool keep_own =
@@ -397,57 +396,67 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
       // the same in every wave. The first kept tile of a split always takes it.
       if (__ballot(m_run > m_ref + kRescaleSlack || m_run_o > m_ref_o + kRescaleSlack) != 0ull) {
         const float alpha = exp2_fast(m_ref - ((m_run == -INFINITY) ? 0.f : m_run));
+        const float alpha_o = exp2_fast(m_ref_o - ((m_run_o == -INFINITY) ? 0.f : m_run_o));
         l_part *= alpha;
+        const float a0 = rg == 0 ? alpha : alpha_o, a1 = rg == 0 ? alpha_o : alpha;
 #pragma unroll
-        for (int db = 0; db < kDvBlocks; ++db) oacc[db] *= alpha;
+        for (int db = 0; db < kDvBlocks; ++db) {
+          oacc[0][db] *= a0;
+          oacc[1][db] *= a1;
+        }
         m_ref = m_run;
         m_ref_o = m_run_o;
-        ps = make_p(sacc, pf);
+        ps = make_p(sacc);
         __syncthreads();
       }
       l_part += ps;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) pf[2 + h2] = sP[wv ^ 2][h2][lane];
-      pv(pf, j & 1);
+      pv(j & 1);
     }
   }
 
-  // Epilogue: the row sum is split over the two key halves of a wave pair (both scaled to the
-  // same m_ref); normalised O (this wave's 256 columns) or the split's partial, and LSE.
+  // Epilogue: the row sum of a row group is split over the key halves of its two waves (both
+  // scaled to the same m_ref); normalised O (this wave's 128 columns of all 64 rows) or the
+  // split's partial, and LSE.
   const float l_mine = sum_halves(l_part);
   if (hh == 0) sL[wv][n] = l_mine;
   __syncthreads();
-  const float l_tot = l_mine + sL[wv ^ 2][n];
-  if (row_ok) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int h = h0 + 32 * rb + n;
+    if (!(h < p.Hq && 32 * rb + n < p.block_r)) continue;
+    const float l_tot = sL[rb][n] + sL[rb + 2][n];
+    const float m_rb = rb == rg ? m_ref : m_ref_o;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (p.num_splits == 1) {
-      __bf16 *orow = (__bf16 *)p.o + b * p.o_sb + (int64_t)my_h * p.o_sh + 256 * kh;
+      __bf16 *orow = (__bf16 *)p.o + b * p.o_sb + (int64_t)h * p.o_sh + 128 * wv;
 #pragma unroll
       for (int db = 0; db < kDvBlocks; ++db) {
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig) {
           const int d0 = db * 32 + 8 * ig + 4 * hh;
           typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-          bf16x4_t ov = {(__bf16)(oacc[db][4 * ig + 0] * inv), (__bf16)(oacc[db][4 * ig + 1] * inv),
-                         (__bf16)(oacc[db][4 * ig + 2] * inv), (__bf16)(oacc[db][4 * ig + 3] * inv)};
+          const f32x16_t &oa = oacc[rb][db];
+          bf16x4_t ov = {(__bf16)(oa[4 * ig + 0] * inv), (__bf16)(oa[4 * ig + 1] * inv),
+                         (__bf16)(oa[4 * ig + 2] * inv), (__bf16)(oa[4 * ig + 3] * inv)};
           *(bf16x4_t *)(orow + d0) = ov;
         }
       }
-      if (p.lse && hh == 0 && kh == 0)
-        p.lse[(int64_t)b * p.Hq + my_h] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+      if (p.lse && hh == 0 && wv == 0)
+        p.lse[(int64_t)b * p.Hq + h] = l_tot > 0.f ? (m_rb + __log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
-      const int64_t row = ((int64_t)b * p.Hq + my_h) * p.num_splits + split;
-      float *op = p.o_part + row * kDv + 256 * kh;
+      const int64_t row = ((int64_t)b * p.Hq + h) * p.num_splits + split;
+      float *op = p.o_part + row * kDv + 128 * wv;
 #pragma unroll
       for (int db = 0; db < kDvBlocks; ++db) {
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig) {
           const int d0 = db * 32 + 8 * ig + 4 * hh;
-          *(float4 *)(op + d0) = make_float4(oacc[db][4 * ig + 0] * inv, oacc[db][4 * ig + 1] * inv,
-                                             oacc[db][4 * ig + 2] * inv, oacc[db][4 * ig + 3] * inv);
+          const f32x16_t &oa = oacc[rb][db];
+          *(float4 *)(op + d0) = make_float4(oa[4 * ig + 0] * inv, oa[4 * ig + 1] * inv,
+                                             oa[4 * ig + 2] * inv, oa[4 * ig + 3] * inv);
         }
       }
-      if (hh == 0 && kh == 0) p.lse_part[row] = l_tot > 0.f ? m_ref + __log2f(l_tot) : -INFINITY;
+      if (hh == 0 && wv == 0) p.lse_part[row] = l_tot > 0.f ? m_rb + __log2f(l_tot) : -INFINITY;
     }
   }
   if (bookkeeper) {
