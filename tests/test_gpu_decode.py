@@ -161,6 +161,18 @@ def test_mla_small_lengths_and_splits():
                  cluster_len=128) > 0
 
 
+@pytest.mark.parametrize("Hq", [16, 40, 100])
+def test_mla_partial_head_blocks(Hq):
+    """MLA with head counts that leave row groups empty (16: the second 32-head group of the only
+    block), half full (40) or a partial second block (100: heads 64..99): every wave's P.V
+    covers both row groups of its block, so invalid rows must neither leak into valid ones nor be
+    written."""
+    L = 600
+    lams = [0.0, 16 / L, 1.0]
+    assert _case(2, Hq, 1, L, 576, [600, 257], lams, (1, 3), 16.0, True, seed=3300 + Hq, Dv=512,
+                 cluster_len=128) > 0
+
+
 def test_gqa_sliding_window_lengths_and_splits():
     """Sliding windows of one key, shorter than a tile, and a few tiles not a multiple of the
     tile, on ragged lengths (one sequence shorter than the window), unsplit and split."""

@@ -53,7 +53,7 @@ def _decode_case(seed):
     rng = random.Random(seed)
     mla = rng.random() < 0.3
     if mla:
-        Hkv, Hq, D, Dv = 1, rng.choice([64, 128]), 576, 512
+        Hkv, Hq, D, Dv = 1, rng.choice([16, 40, 64, 100, 128]), 576, 512
     else:
         Hkv = rng.choice([1, 2, 4])
         Hq = Hkv * rng.choice([1, 3, 4, 8, 16])
