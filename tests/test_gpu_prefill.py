@@ -102,6 +102,35 @@ def test_tiny_fp32_mha_all_lambdas():
     assert _case(1, 512, 2, 2, 64, torch.float32, False, 64, 8.0, lams, seed=1001)
 
 
+@pytest.mark.parametrize("dtype,D,block_r,lq,lkv", [
+    (torch.bfloat16, 128, 128, 300, 1000),
+    (torch.bfloat16, 128, 128, 1000, 77),
+    (torch.bfloat16, 64, 64, 129, 700),
+    (torch.float32, 64, 64, 200, 513),
+])
+def test_cross_length_non_causal(dtype, D, block_r, lq, lkv):
+    """Non-causal prefill with Lq != Lkv (cross attention), including a key range shorter than
+    one query block; q, k and v are row slices of longer tensors (strided views)."""
+    need_gpu()
+    B, Hq, Hkv = 2, 8, 2
+    q, k, v = prefill_inputs(B=B, L=max(lq, lkv), Hq=Hq, Hkv=Hkv, d=D, cluster_len=64,
+                             dtype=dtype, seed=5100 + lq, beta=16.0)
+    q, k, v = q[:, :lq], k[:, :lkv], v[:, :lkv]
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    skipped = 0
+    for lam in (0.0, 16 / lkv, 1.0):
+        what = f"cross prefill {dtype} d{D} br{block_r} Lq{lq} Lkv{lkv} lam={lam}"
+        print(what, flush=True)
+        res = _run_gpu(qd, kd, vd, causal=False, lam=lam, block_r=block_r)
+        ref = oracle.prefill(q, k, v, causal=False, block_r=res["br"], block_c=res["bc"],
+                             scale=oracle_scale(D), lam=lam, threads=8)
+        _, band_mism, _ = _check_units(res, ref, q, k, v, False, lam, what)
+        assert res["counters"][0] == ref.visited
+        assert abs(res["counters"][1] - ref.skipped) <= band_mism
+        skipped += ref.skipped
+    assert skipped > 0
+
+
 @pytest.mark.parametrize("block_r", [128, 64, 32])
 def test_bf16_causal_gqa_ragged(block_r):
     L = 700

@@ -142,6 +142,26 @@ def test_prefill_lambda_zero_matches_torch_sdpa(causal):
         assert u.visited == expect
 
 
+@pytest.mark.parametrize("lq,lkv", [(70, 150), (150, 37)])
+def test_cross_length_prefill_lambda_zero_matches_torch_sdpa(lq, lkv):
+    """Non-causal prefill with fewer or more queries than keys (cross attention): every query
+    row sees all Lkv keys; the last key tile is ragged."""
+    from flashattention_softmax_threshold_amd.inputs import prefill_inputs
+
+    B, Hq, Hkv, d = 2, 4, 2, 16
+    q, k, v = prefill_inputs(B=B, L=max(lq, lkv), Hq=Hq, Hkv=Hkv, d=d, cluster_len=32,
+                             dtype=torch.float32, seed=4, beta=4.0)
+    q, k, v = q[:, :lq], k[:, :lkv], v[:, :lkv]
+    res = oracle.prefill(q, k, v, causal=False, block_r=32, block_c=16, scale=1 / math.sqrt(d),
+                         lam=0.0)
+    ref = _sdpa(q.numpy(), k.numpy(), v.numpy(), False)
+    assert len(res.units) == B * Hq * (-(-lq // 32))
+    for (b, h, qb), u in res.units.items():
+        r0 = qb * 32
+        np.testing.assert_allclose(u.o, ref[b, r0:r0 + u.o.shape[0], h], rtol=1e-10, atol=1e-11)
+        assert u.visited == -(-lkv // 16) and u.skipped == 0
+
+
 def test_decode_lambda_zero_matches_torch_sdpa_with_lengths_and_splits():
     from flashattention_softmax_threshold_amd.inputs import decode_inputs
 
