@@ -400,7 +400,11 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
     mask_tile(j, cur);
     if (keep_prev) {
       rescale_to(m_prev);
+      // A wave in its exponential / P.V phase issues ahead of a wave of the same SIMD that is
+      // still scoring: about 1 % faster than equal priorities.
+      __builtin_amdgcn_s_setprio(1);
       exp_pv(prev, (j - 1) & 1);
+      __builtin_amdgcn_s_setprio(0);
     }
     publish_margin(j, vote_tile(j, cur));
   };
