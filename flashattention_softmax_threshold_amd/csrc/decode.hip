@@ -51,8 +51,11 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 &u, float *f) {
 
 // Two workgroups per CU (at most 256 registers per wave): twice the K and V loads in flight, which
 // the skip case (V requested only after the vote) and the paged cache (page-number reads) need.
+// At d = 128 with 8 or 16 rows per tile the O accumulators do not fit in 256 registers (spills of
+// 24-388 bytes per lane), and one workgroup per CU without spills is 14-44 % faster; at d = 64 with
+// 16 rows the small spill at two workgroups per CU costs less than halving the loads in flight.
 template <int D, int RB, bool PAGED>
-__global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, (D == 128 && RB > 4) ? 1 : 2) void decode_gqa_kernel(DecodeParams p) {
   constexpr int STEPS = D / 32;  // k-steps of one 16x16x32 MFMA chain
   constexpr int CPR = D / 8;     // 16-byte chunks per key row
   constexpr int KPI = 64 / CPR;  // keys covered by one V load instruction
