@@ -14,13 +14,17 @@
 //      round, so K stays in flight while this round finishes;
 //   2. tile row maxima meet in LDS; every wave forms the same running (prefix) maxima over the 4
 //      tiles in key order, the same per-tile votes and the round maximum M;
-//   3. a wave whose tile is kept requests its V tile only now, writes P = exp2(S - M) to LDS and
-//      accumulates O += P V on the vector ALUs (16-byte V loads, one 8-column slice per lane);
-//      skipped tiles load no V at all;
+//   3. a wave whose tile is kept requests its V tile only now, straight from HBM into its own LDS
+//      tile (global_load_lds_dwordx4); skipped tiles load no V at all. It forms P = exp2(S - M)
+//      in bf16 from its score registers, which are already the B operand layout of
+//      v_mfma_f32_16x16x32_bf16, and accumulates O^T += V^T P^T on the matrix cores, V^T read
+//      from the LDS tile with ds_read_b64_tr_b16 (16 MFMAs per tile at d = 128 for any number of
+//      rows; the same product on the vector ALUs would take rows x d x 64 multiply-adds);
 //   4. at the end the 4 waves' partial O and l are summed through LDS.
 // Using the round maximum M for P (instead of re-scaling tile by tile) is the same online
 // softmax in exact arithmetic; the skip decisions use each tile's own prefix maximum.
 #include "internal.h"
+#include "lds_dma.h"
 
 #include <math.h>
 
@@ -29,6 +33,9 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -40,31 +47,29 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ void bf16x8_to_f32(const uint4 &u, float *f) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-
-// Two workgroups per CU (at most 256 registers per wave): twice the K and V loads in flight, which
-// the skip case (V requested only after the vote) and the paged cache (page-number reads) need.
-// At d = 128 with 8 or 16 rows per tile the O accumulators do not fit in 256 registers (spills of
-// 24-388 bytes per lane), and one workgroup per CU without spills is 14-44 % faster; at d = 64 with
-// 16 rows the small spill at two workgroups per CU costs less than halving the loads in flight.
+// Two workgroups per CU (at most 256 registers per wave; about 200 are used at d = 128 for any
+// number of rows, since O lives in 16x16 MFMA accumulators): twice the K and V loads in flight,
+// which the skip case (V requested only after the vote) and the paged cache (page-number reads)
+// need.
 template <int D, int RB, bool PAGED>
-__global__ __launch_bounds__(256, (D == 128 && RB > 4) ? 1 : 2) void decode_gqa_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
   constexpr int STEPS = D / 32;  // k-steps of one 16x16x32 MFMA chain
   constexpr int CPR = D / 8;     // 16-byte chunks per key row
-  constexpr int KPI = 64 / CPR;  // keys covered by one V load instruction
-  constexpr int VL = 64 / KPI;   // V loads per lane per tile
+  constexpr int ROWB = 2 * D;    // bytes of a key row
+  constexpr int RPL = 1024 / ROWB;            // V rows one wave-wide 16-byte copy fills
+  constexpr int VLD = kBlockC / RPL;          // V copies per wave per tile
+  constexpr int RPB = 256 / ROWB;             // key rows per 256 bytes of LDS banks
+  // Each wave's V tile (64 keys x D, bf16) in LDS, 16-byte chunks XOR-swizzled by the row; the
+  // same memory holds the waves' partial O for the final sum.
+  __shared__ __attribute__((aligned(1024))) char sV[4][kBlockC * ROWB];
+  static_assert(sizeof(float) * 4 * RB * D <= sizeof(sV), "partial O must fit in the V tiles");
+  float(*sO)[RB][D] = reinterpret_cast<float(*)[RB][D]>(&sV[0][0]);
   __shared__ float sT[2][4][16];
-  __shared__ __attribute__((aligned(16))) float sP[4][64][RB];
-  __shared__ __attribute__((aligned(16))) float sO[4][RB][D];
   __shared__ float sL[4][16];
   __shared__ float sM[16];
+  // Chunk c of key row r sits at chunk c ^ vswz(r): 8 consecutive rows reading the same
+  // 32-byte column window (a transposing read) cover all 64 banks.
+  auto vswz = [&](int r) { return 2 * ((r / RPB) % (CPR / 2)); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -145,17 +150,33 @@ __global__ __launch_bounds__(256, (D == 128 && RB > 4) ? 1 : 2) void decode_gqa_
     }
   };
 
-  float o[RB][8];
+  // O^T = V^T P^T on the matrix cores: oacc[db] holds head dims 16 db + 4 kgrp .. + 3 of query
+  // row n (16x16 output blocks).
+  f32x4_t oacc[D / 16];
 #pragma unroll
-  for (int r = 0; r < RB; ++r)
+  for (int db = 0; db < D / 16; ++db) oacc[db] = (f32x4_t)0.f;
+  // V copy of load kk: lane L fills row kk * RPL + L / CPR at physical chunk L % CPR with logical
+  // chunk (L % CPR) ^ vswz(row); keys past the sequence copy its last row (their P is 0).
+  const uint32_t sv_base = lds_addr(&sV[wv][0]);
+  auto load_v = [&](int t, int pages) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+    for (int kk = 0; kk < VLD; ++kk) {
+      const int r = kk * RPL + lane / CPR;
+      const int key = min(t * kBlockC + r, seq_len - 1);
+      const int64_t off = row_off(key, pages, p.v_sb, p.v_ss);
+      lds_dma16(Vg + off + 8 * ((lane % CPR) ^ vswz(r)), sv_base + kk * 1024);
+    }
+  };
+  // Transposing V reads: for k-step ks (keys 32 ks ..) and column block db, source lane L points at
+  // key 32 ks + 4 (L / 16) + (L % 16) / 4 (+ 16 for the second read), head dims
+  // 16 db + 4 (L % 4) .. + 3; lane L then receives head dim 16 db + L % 16 at the keys
+  // 32 ks + 4 (L / 16) + 0..3 (and + 16), the key order of the P fragments.
+  const int tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2);
+  const int tr_cb = lane & 3;
   float l_part = 0.f;
   float m_run = -INFINITY;
   unsigned visited = 0, skipped = 0;
   const int n_rounds = t_end > t_begin ? (t_end - t_begin + 3) / 4 : 0;
-  const int vc = lane % CPR;   // V column chunk of this lane
-  const int vk = lane / CPR;   // V key offset of this lane inside a load instruction
 
   if (n_rounds > 0 && t_begin + wv < t_end) {
     pages_cur = page_of_lane_key(t_begin + wv);
@@ -218,61 +239,54 @@ __global__ __launch_bounds__(256, (D == 128 && RB > 4) ? 1 : 2) void decode_gqa_
     const float M = mp;
     const bool my_keep = have && keep_w[wv];
 
-    // V tile only for a kept tile.
-    uint4 vreg[VL];
-    if (my_keep) {
-#pragma unroll
-      for (int kk = 0; kk < VL; ++kk) {
-        const int key = t * kBlockC + kk * KPI + vk;
-        const int64_t off = row_off(key, pages_cur, p.v_sb, p.v_ss);
-        vreg[kk] = key < seq_len ? *(const uint4 *)(Vg + off + 8 * vc) : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
+    // V tile only for a kept tile, straight into this wave's LDS tile.
+    if (my_keep) load_v(t, pages_cur);
     const float M_use = (M == -INFINITY) ? 0.f : M;
     const float alpha = exp2_fast(m_run - M_use);  // for this lane's row n
     l_part *= alpha;
-    // O is held column-wise (every lane has all rows): row rr's factor comes from lane rr.
 #pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const float a_r = __shfl(alpha, rr);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[rr][e] *= a_r;
-    }
+    for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
 
     if (my_keep) {
-      float ps = 0.f;
+      // P = exp2(S - M) in bf16 as the B operands of the two 32-key k-steps: elements 0..3 are
+      // the keys of block 2 ks, 4..7 those of block 2 ks + 1 (this lane's 4 keys of each).
       const bool row_live = n < nrows;
+      const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+      bf16x8_t pb[2];
+      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = row_live ? exp2_fast(fmaf(sacc[kb][i], p.scale_log2, -M_use)) : 0.f;
-          ps += pv;
-          if (n < RB) sP[wv][16 * kb + 4 * kgrp + i][n] = pv;
+        for (int e = 0; e < 8; ++e) {
+          const float x = sacc[2 * ks + (e >> 2)][e & 3];
+          pb[ks][e] = (__bf16)(row_live ? exp2_fast(fmaf(x, p.scale_log2, -M_use)) : 0.f);
+        }
+        const bf16x2_t x0 = {pb[ks][0], pb[ks][1]}, x1 = {pb[ks][2], pb[ks][3]};
+        const bf16x2_t x2 = {pb[ks][4], pb[ks][5]}, x3 = {pb[ks][6], pb[ks][7]};
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(x0, one, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(x1, one, ps1, false);
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(x2, one, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, ps1, false);
+      }
+      l_part += ps0 + ps1;
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's V copies have landed in its LDS tile
+      wave_lds_sync();
+      const char *vt = &sV[wv][0];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          const int r0 = 32 * ks + tr_row, r1 = r0 + 16;
+          const int c = 2 * db + (tr_cb >> 1);
+          const char *p0 = vt + r0 * ROWB + 16 * (c ^ vswz(r0)) + 8 * (tr_cb & 1);
+          const char *p1 = vt + r1 * ROWB + 16 * (c ^ vswz(r1)) + 8 * (tr_cb & 1);
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
+          const bf16x8_t va =
+              __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ks], oacc[db], 0, 0, 0);
         }
       }
-      l_part += ps;
-      wave_lds_sync();
-#pragma unroll
-      for (int kk = 0; kk < VL; ++kk) {
-        const int kl = kk * KPI + vk;
-        float pr[RB];
-#pragma unroll
-        for (int q4 = 0; q4 < RB / 4; ++q4) {
-          const float4 x = *(const float4 *)(&sP[wv][kl][4 * q4]);
-          pr[4 * q4 + 0] = x.x;
-          pr[4 * q4 + 1] = x.y;
-          pr[4 * q4 + 2] = x.z;
-          pr[4 * q4 + 3] = x.w;
-        }
-        float vf[8];
-        bf16x8_to_f32(vreg[kk], vf);
-#pragma unroll
-        for (int rr = 0; rr < RB; ++rr)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[rr][e] = fmaf(pr[rr], vf[e], o[rr][e]);
-      }
-      wave_lds_sync();
     }
     m_run = M;
     if constexpr (PAGED) pages_cur = pages_next;
@@ -292,21 +306,12 @@ __global__ __launch_bounds__(256, (D == 128 && RB > 4) ? 1 : 2) void decode_gqa_
   }
 
   // ---- Sum the waves' partials; write O (unsplit) or the split's partial.
+  __syncthreads();  // every wave's last V reads are done: the V tiles become sO
+  if (n < RB) {
 #pragma unroll
-  for (int rr = 0; rr < RB; ++rr) {
+    for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = o[rr][e];
-#pragma unroll
-      for (int off = CPR; off < 64; off <<= 1) v += __shfl_xor(v, off);
-      o[rr][e] = v;
-    }
-  }
-  if (lane < CPR) {
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sO[wv][rr][8 * lane + e] = o[rr][e];
+      for (int i = 0; i < 4; ++i) sO[wv][n][16 * db + 4 * kgrp + i] = oacc[db][i];
   }
   float lrow = l_part;
   lrow += __shfl_xor(lrow, 16);
