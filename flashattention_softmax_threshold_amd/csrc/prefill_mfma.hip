@@ -400,11 +400,13 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
     mask_tile(j, cur);
     if (keep_prev) {
       rescale_to(m_prev);
-      // A wave in its exponential / P.V phase issues ahead of a wave of the same SIMD that is
-      // still scoring: about 1 % faster than equal priorities.
-      __builtin_amdgcn_s_setprio(1);
+      // Two heads per workgroup: a wave in its exponential / P.V phase issues ahead of the other
+      // head's wave on the same SIMD that is still scoring (about 1 % faster). With one head
+      // per workgroup the two waves of a SIMD belong to different workgroups, and the same
+      // priority costs 5 % at lambda = 0 (Video-DiT), so it is not raised there.
+      if constexpr (NH == 2) __builtin_amdgcn_s_setprio(1);
       exp_pv(prev, (j - 1) & 1);
-      __builtin_amdgcn_s_setprio(0);
+      if constexpr (NH == 2) __builtin_amdgcn_s_setprio(0);
     }
     publish_margin(j, vote_tile(j, cur));
   };
