@@ -369,14 +369,25 @@ __global__ __launch_bounds__(128) void split_combine_kernel(DecodeParams p, int 
     const float x = p.lse_part[row0 + s];
     if (x > -INFINITY) wsum += exp2_fast(x - M);
   }
-  for (int d = threadIdx.x; d < dv; d += blockDim.x) {
-    float acc = 0.f;
+  // dv is 64, 128 or 512: each thread merges 4 consecutive columns with 16-byte reads.
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  for (int d = 4 * (int)threadIdx.x; d < dv; d += 4 * (int)blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < S; ++s) {
       const float x = p.lse_part[row0 + s];
-      if (x > -INFINITY) acc = fmaf(exp2_fast(x - M), p.o_part[(row0 + s) * dv + d], acc);
+      if (x > -INFINITY) {
+        const float w = exp2_fast(x - M);
+        const float4 v = *(const float4 *)(p.o_part + (row0 + s) * dv + d);
+        acc.x = fmaf(w, v.x, acc.x);
+        acc.y = fmaf(w, v.y, acc.y);
+        acc.z = fmaf(w, v.z, acc.z);
+        acc.w = fmaf(w, v.w, acc.w);
+      }
     }
-    ((__bf16 *)p.o)[b * p.o_sb + (int64_t)h * p.o_sh + d] =
-        (__bf16)(M > -INFINITY ? acc / wsum : 0.f);
+    const bool any = M > -INFINITY;
+    const bf16x4_t ov = {(__bf16)(any ? acc.x / wsum : 0.f), (__bf16)(any ? acc.y / wsum : 0.f),
+                         (__bf16)(any ? acc.z / wsum : 0.f), (__bf16)(any ? acc.w / wsum : 0.f)};
+    *(bf16x4_t *)((__bf16 *)p.o + b * p.o_sb + (int64_t)h * p.o_sh + d) = ov;
   }
   if (threadIdx.x == 0 && p.lse)
     p.lse[(int64_t)b * p.Hq + h] = M > -INFINITY ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
