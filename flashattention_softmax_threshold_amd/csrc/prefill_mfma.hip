@@ -94,10 +94,12 @@ struct Geo {
 __device__ __forceinline__ int swz_k(int row, int cpr) { return row & (cpr - 1); }
 __device__ __forceinline__ int swz_v(int row, int cpr) { return (4 * (row & 3)) & (cpr - 1); }
 
-// NH query heads of one KV group per workgroup (4 waves, i.e. one 128-row unit, per head): the
-// K and V tiles in LDS serve all NH heads, so each wave issues 1 / NH of the loads. WIN: the
-// call has a sliding window (a separate instance, so calls without one pay nothing for it).
-template <int D, int NH, bool WIN>
+// NH units per workgroup (4 waves, i.e. one 128-row unit, each) that read the same K and V
+// tiles: NH query heads of one KV group at one query block, or, with QP (non-causal calls only),
+// one query head at two neighbouring query blocks. The K and V tiles in LDS serve all NH units,
+// so each wave issues 1 / NH of the loads. WIN: the call has a sliding window (a separate
+// instance, so calls without one pay nothing for it).
+template <int D, int NH, bool WIN, bool QP>
 __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillParams p) {
   using G = Geo<D, NH>;
   constexpr int RB = G::ROW_BYTES, CPR = G::CPR;
@@ -115,19 +117,23 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
 
   // ---- Which unit: XCD-aware numbering (see the header comment).
   const int grp = p.Hq / p.Hkv;
-  const int gw = grp / NH;  // workgroups per (KV head, query block)
-  const int n_units = p.B * p.Hkv * gw * p.n_qblocks;
+  const int gw = QP ? grp : grp / NH;  // workgroups per (KV head, query block or block pair)
+  const int n_qw = QP ? (p.n_qblocks + 1) / 2 : p.n_qblocks;  // query blocks (pairs) per head
+  const int n_units = p.B * p.Hkv * gw * n_qw;
   int u = (int)blockIdx.x;
   if ((n_units & 7) == 0) u = (u & 7) * (n_units >> 3) + (u >> 3);
-  const int per_kv = gw * p.n_qblocks;
+  const int per_kv = gw * n_qw;
   const int bg = u / per_kv;          // b * Hkv + g
   const int t = u - bg * per_kv;
   const int qb_r = t / gw;
   const int hl = t - qb_r * gw;
   const int b = bg / p.Hkv;
   const int g = bg - b * p.Hkv;
-  const int hq = g * grp + hl * NH + hs;
-  const int qb = p.causal ? (p.n_qblocks - 1 - qb_r) : qb_r;
+  const int hq = QP ? g * grp + hl : g * grp + hl * NH + hs;
+  const int qb = QP ? 2 * qb_r + hs : (p.causal ? (p.n_qblocks - 1 - qb_r) : qb_r);
+  // QP with an odd number of query blocks: the last pair's second unit does not exist (its rows
+  // are all past Lq); its waves take part in the loads and barriers but record nothing.
+  const bool unit_ok = qb < p.n_qblocks;
 
   const __bf16 *__restrict__ Qg = (const __bf16 *)p.q + b * p.q_sb + hq * p.q_sh;
   const __bf16 *__restrict__ Kg = (const __bf16 *)p.k + b * p.k_sb + g * p.k_sh;
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
 
   // The four votes of this head's unit (one 16-byte LDS read) and the unit's decision; the first
   // lane of the unit's first wave keeps its counts and observation outputs.
-  const bool bookkeeper = wq == 0 && lane == 0;
+  const bool bookkeeper = wq == 0 && lane == 0 && unit_ok;
   auto read_votes = [&](int j) { return *(const int4 *)&sVote[j & 1][kNW * hs]; };
   auto decision = [&](int j, int4 vt) {
     const int keep = vt.x | vt.y | vt.z | vt.w;
@@ -480,18 +486,31 @@ template <int D, int NH>
 void launch_nh(const PrefillParams &p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.B * p.Hq / NH * p.n_qblocks));
   if (p.window > 0)
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, true>), grid, dim3(kNT * NH), 0, stream, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, true, false>), grid, dim3(kNT * NH), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, false>), grid, dim3(kNT * NH), 0, stream, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, false, false>), grid, dim3(kNT * NH), 0, stream,
+                       p);
+}
+
+// Non-causal calls whose query heads do not pair up: two neighbouring query blocks of one head
+// per workgroup.
+template <int D>
+void launch_qp(const PrefillParams &p, hipStream_t stream) {
+  const dim3 grid((unsigned)(p.B * p.Hq * ((p.n_qblocks + 1) / 2)));
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, 2, false, true>), grid, dim3(kNT * 2), 0, stream, p);
 }
 
 // Two heads per workgroup when the query heads of a KV head pair up (even group), else one.
 hipError_t launch_prefill_mfma(const PrefillParams &p, int head_dim, hipStream_t stream) {
   const bool pair = (p.Hq / p.Hkv) % 2 == 0;
+  const bool qpair = !pair && !p.causal && p.window == 0 && p.n_qblocks > 1;
   if (head_dim == 128)
-    pair ? launch_nh<128, 2>(p, stream) : launch_nh<128, 1>(p, stream);
+    pair ? launch_nh<128, 2>(p, stream)
+         : (qpair ? launch_qp<128>(p, stream) : launch_nh<128, 1>(p, stream));
   else if (head_dim == 64)
-    pair ? launch_nh<64, 2>(p, stream) : launch_nh<64, 1>(p, stream);
+    pair ? launch_nh<64, 2>(p, stream)
+         : (qpair ? launch_qp<64>(p, stream) : launch_nh<64, 1>(p, stream));
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

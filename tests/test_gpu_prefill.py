@@ -140,6 +140,16 @@ def test_bf16_causal_gqa_ragged(block_r):
                  cluster_len=128, sinks=16)
 
 
+@pytest.mark.parametrize("L,Hq,Hkv,D", [(300, 3, 3, 128), (513, 3, 1, 128), (640, 2, 2, 64),
+                                         (129, 1, 1, 128)])
+def test_bf16_noncausal_query_block_pairs(L, Hq, Hkv, D):
+    """Non-causal calls whose query heads do not pair up run two neighbouring 128-row query
+    blocks of one head per workgroup; an odd block count leaves the last pair's second unit
+    empty (it must record nothing), an even one fills every pair."""
+    assert _case(2, L, Hq, Hkv, D, torch.bfloat16, False, 128, 16.0, [0.0, 16 / L, 1.0],
+                 seed=5200 + L + Hq, cluster_len=64)
+
+
 def test_bf16_noncausal_d64_and_fp32_causal_d128():
     assert _case(1, 333, 4, 4, 64, torch.bfloat16, False, 128, 16.0, [0.0, 0.01, 0.3], seed=9)
     assert _case(1, 200, 2, 1, 128, torch.float32, True, 64, 16.0, [0.0, 0.05], seed=10)
