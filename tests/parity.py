@@ -3,9 +3,11 @@
 Bar (bf16 inputs, fp32 accumulation): max|dO| <= 1e-2 * max|O| against the exact oracle and
 mean|dO| <= 1e-3 against the oracle rounded to the output dtype (bf16 rounding of an output of
 magnitude ~1 alone is ~1e-3 on average); LSE within 1e-2 (natural log). fp32 inputs: max|dO| <= 1e-4 * max|O|,
-mean|dO| <= 1e-5, LSE within 1e-4 + 2e-6 |LSE|: the LSE is about the largest scaled score, which
-the kernel forms in fp32, so its rounding grows with the score's magnitude (an fp32 ulp at 256 is
-3e-5). Skip decisions must agree exactly on every tile whose oracle
+mean|dO| <= 1e-5 + 1e-7 max|LSE|, LSE within 1e-4 + 2e-6 |LSE|: the LSE is about the largest
+scaled score, which the kernel forms in fp32, so its rounding grows with the score's magnitude
+(an fp32 ulp at 256 is 3e-5); the exponent of every P carries that absolute rounding (about
+6e-8, one ulp per unit, times the score), so the outputs' mean error grows with it too. Skip
+decisions must agree exactly on every tile whose oracle
 margin lies outside a band around ln(lambda); inside the band float rounding may flip the
 decision, and such tiles are counted, not failed (their units are then compared against the
 oracle evaluated with the kernel's decisions).
@@ -20,8 +22,8 @@ import torch
 
 MARGIN_BAND = 1e-3
 TOL = {
-    torch.bfloat16: dict(max_rel=1e-2, mean_abs=1e-3, lse_abs=1e-2, lse_rel=0.0),
-    torch.float32: dict(max_rel=1e-4, mean_abs=1e-5, lse_abs=1e-4, lse_rel=2e-6),
+    torch.bfloat16: dict(max_rel=1e-2, mean_abs=1e-3, mean_lse=0.0, lse_abs=1e-2, lse_rel=0.0),
+    torch.float32: dict(max_rel=1e-4, mean_abs=1e-5, mean_lse=1e-7, lse_abs=1e-4, lse_rel=2e-6),
 }
 
 
@@ -38,17 +40,26 @@ def _round_to(x: np.ndarray, dtype) -> np.ndarray:
     return torch.as_tensor(x, dtype=torch.float64).to(dtype).to(torch.float64).numpy()
 
 
-def assert_outputs_close(o_gpu: np.ndarray, o_ref: np.ndarray, dtype, what: str):
+def assert_outputs_close(o_gpu: np.ndarray, o_ref: np.ndarray, dtype, what: str,
+                         lse_ref: np.ndarray | None = None):
     """max|dO| against the exact oracle; mean|dO| against the oracle rounded to the output dtype
-    (a bf16 output of magnitude ~1 carries ~1e-3 of rounding on its own, whatever computed it)."""
+    (a bf16 output of magnitude ~1 carries ~1e-3 of rounding on its own, whatever computed it).
+    lse_ref: the oracle's LSE of the same rows, whose largest magnitude sets the fp32 part of the
+    mean bar that grows with the scores."""
     tol = TOL[dtype]
+    lse_mag = 0.0
+    if lse_ref is not None:
+        fin = np.isfinite(lse_ref)
+        lse_mag = float(np.abs(lse_ref[fin]).max()) if fin.any() else 0.0
+    mean_tol = tol["mean_abs"] + tol["mean_lse"] * lse_mag
     err = np.abs(o_gpu - o_ref)
     scale = np.abs(o_ref).max()
     assert np.isfinite(o_gpu).all(), f"{what}: non-finite output"
     assert err.max() <= tol["max_rel"] * scale, \
         f"{what}: max|dO| {err.max():.3e} > {tol['max_rel']} * max|O| ({scale:.3e})"
     mean_err = np.abs(o_gpu - _round_to(o_ref, dtype)).mean()
-    assert mean_err <= tol["mean_abs"], f"{what}: mean|dO| {mean_err:.3e} (vs rounded oracle)"
+    assert mean_err <= mean_tol, \
+        f"{what}: mean|dO| {mean_err:.3e} > {mean_tol:.3e} (vs rounded oracle)"
     return float(err.max()), float(mean_err)
 
 

@@ -73,7 +73,8 @@ def _check(res, ref, q, k, v, lam, what, kv_len, window=0):
         orf.append(u.o)
         lg.append(lse_gpu[b, h0:h0 + rows])
         lr.append(u.lse)
-    assert_outputs_close(np.concatenate(og), np.concatenate(orf), q.dtype, what)
+    assert_outputs_close(np.concatenate(og), np.concatenate(orf), q.dtype, what,
+                         lse_ref=np.concatenate(lr))
     assert_lse_close(np.concatenate(lg), np.concatenate(lr), q.dtype, what)
     return band_mism
 

@@ -68,7 +68,7 @@ def _check_units(res, ref, q, k, v, causal, lam, what, window=0):
         lg.append(lse_gpu[b, h, r0:r0 + rows])
         lr.append(u.lse)
     o_g, o_r = np.concatenate(og), np.concatenate(orf)
-    err = assert_outputs_close(o_g, o_r, q.dtype, what)
+    err = assert_outputs_close(o_g, o_r, q.dtype, what, lse_ref=np.concatenate(lr))
     assert_lse_close(np.concatenate(lg), np.concatenate(lr), q.dtype, what)
     return err, band_mism, band
 
