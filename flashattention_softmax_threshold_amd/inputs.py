@@ -66,7 +66,8 @@ def prefill_inputs(*, B: int, L: int, Hq: int, Hkv: int, d: int, cluster_len: in
         if centres_all is None:
             raise ValueError("sinks are defined for the plain clustered recipe")
         sink = 3.0 * centres_all.mean(dim=2, keepdim=True)  # [B, Hkv, 1, d]
-        k[:, :, :sinks, :] = sink.expand(B, Hkv, sinks, d)
+        ns = min(sinks, L)  # a sequence shorter than the sink count is all sinks
+        k[:, :, :ns, :] = sink.expand(B, Hkv, ns, d)
     grp = Hq // Hkv
     q_centre = centre.repeat_interleave(grp, dim=1)  # [B, Hq, L, d]
     q = q_centre + 0.5 * _randn((B, Hq, L, d), g, device)

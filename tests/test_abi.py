@@ -280,3 +280,19 @@ def test_fit_calibration_matches_oracle_and_refuses_bad_input():
         F.blasst_sparsity_curve([0.0], [7], [0.5])                          # unknown status
     with pytest.raises(F.BlasstError):
         F.blasst_sparsity_curve([0.0], [0], [-1.0])                         # negative lambda
+
+
+def test_generator_sinks_on_a_sequence_shorter_than_the_sink_count():
+    """The seeded clustered generator with more sink keys than keys: every key is a sink
+    (3 x the mean centre, no noise), and longer sequences keep exactly `sinks` of them."""
+    import torch
+    from flashattention_softmax_threshold_amd.inputs import prefill_inputs
+
+    q, k, v = prefill_inputs(B=2, L=5, Hq=4, Hkv=2, d=16, cluster_len=16, dtype=torch.float32,
+                             seed=11, beta=4.0, sinks=8)
+    assert q.shape == (2, 5, 4, 16) and k.shape == (2, 5, 2, 16) and v.shape == (2, 5, 2, 16)
+    assert torch.equal(k, k[:, :1].expand_as(k))
+    q, k, v = prefill_inputs(B=1, L=40, Hq=2, Hkv=1, d=16, cluster_len=16, dtype=torch.float32,
+                             seed=11, beta=4.0, sinks=8)
+    assert torch.equal(k[:, :8], k[:, :1].expand(1, 8, 1, 16))
+    assert not torch.equal(k[:, 8], k[:, 0])
