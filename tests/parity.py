@@ -2,8 +2,9 @@
 
 Bar (bf16 inputs, fp32 accumulation): max|dO| <= 1e-2 * max|O| against the exact oracle and
 mean|dO| <= 1e-3 against the oracle rounded to the output dtype (bf16 rounding of an output of
-magnitude ~1 alone is ~1e-3 on average); LSE within 1e-2 (natural log). fp32 inputs: max|dO| <= 1e-4 * max|O|,
-mean|dO| <= 1e-5 + 1e-7 max|LSE|, LSE within 1e-4 + 2e-6 |LSE|: the LSE is about the largest
+magnitude ~1 alone is ~1e-3 on average); LSE within 1e-2 (natural log). fp32 inputs:
+max|dO| <= (1e-4 + 1e-6 max|LSE|) * max|O|, mean|dO| <= 1e-5 + 1e-7 max|LSE|, LSE within
+1e-4 + 2e-6 |LSE|: the LSE is about the largest
 scaled score, which the kernel forms in fp32, so its rounding grows with the score's magnitude
 (an fp32 ulp at 256 is 3e-5); the exponent of every P carries that absolute rounding (about
 6e-8, one ulp per unit, times the score), so the outputs' mean error grows with it too. Skip
@@ -22,8 +23,10 @@ import torch
 
 MARGIN_BAND = 1e-3
 TOL = {
-    torch.bfloat16: dict(max_rel=1e-2, mean_abs=1e-3, mean_lse=0.0, lse_abs=1e-2, lse_rel=0.0),
-    torch.float32: dict(max_rel=1e-4, mean_abs=1e-5, mean_lse=1e-7, lse_abs=1e-4, lse_rel=2e-6),
+    torch.bfloat16: dict(max_rel=1e-2, max_lse=0.0, mean_abs=1e-3, mean_lse=0.0, lse_abs=1e-2,
+                         lse_rel=0.0),
+    torch.float32: dict(max_rel=1e-4, max_lse=1e-6, mean_abs=1e-5, mean_lse=1e-7, lse_abs=1e-4,
+                        lse_rel=2e-6),
 }
 
 
@@ -52,11 +55,12 @@ def assert_outputs_close(o_gpu: np.ndarray, o_ref: np.ndarray, dtype, what: str,
         fin = np.isfinite(lse_ref)
         lse_mag = float(np.abs(lse_ref[fin]).max()) if fin.any() else 0.0
     mean_tol = tol["mean_abs"] + tol["mean_lse"] * lse_mag
+    max_tol = tol["max_rel"] + tol["max_lse"] * lse_mag
     err = np.abs(o_gpu - o_ref)
     scale = np.abs(o_ref).max()
     assert np.isfinite(o_gpu).all(), f"{what}: non-finite output"
-    assert err.max() <= tol["max_rel"] * scale, \
-        f"{what}: max|dO| {err.max():.3e} > {tol['max_rel']} * max|O| ({scale:.3e})"
+    assert err.max() <= max_tol * scale, \
+        f"{what}: max|dO| {err.max():.3e} > {max_tol:.3e} * max|O| ({scale:.3e})"
     mean_err = np.abs(o_gpu - _round_to(o_ref, dtype)).mean()
     assert mean_err <= mean_tol, \
         f"{what}: mean|dO| {mean_err:.3e} > {mean_tol:.3e} (vs rounded oracle)"
