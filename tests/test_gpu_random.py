@@ -38,7 +38,7 @@ def _prefill_case(seed):
                 cluster_len=rng.choice([16, 64, 128]), sinks=rng.choice([0, 8]))
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(100))
 def test_random_prefill(seed):
     need_gpu()
     c = _prefill_case(9000 + seed)
@@ -72,7 +72,7 @@ def _decode_case(seed):
                 heads_major=rng.random() < 0.5)
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(100))
 def test_random_decode(seed):
     need_gpu()
     c = _decode_case(9100 + seed)
