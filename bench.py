@@ -404,6 +404,40 @@ def _decode_part(F, torch, args, dev, stream, out):
                       "time_vs_contiguous": (msp / ms_c) if ms_c else None})
         _progress(f"decode gqa paged {ps} heads_major={hm}: {msp:.4f} ms")
         del kp, vp, table
+    curve = None
+    if msd0 is not None:
+        # Speedup against skip fraction, as for prefill: thresholds at quantiles of the tile
+        # margins of one lambda = 0 call (a tile is skipped exactly when its margin is below
+        # ln lambda); the bytes ceiling is again 2 / (2 - f) (K always, V of kept tiles).
+        import numpy as np
+
+        n_rb = (D["Hq"] // D["Hkv"] + brd - 1) // brd
+        ntl = (D["L"] + bcd - 1) // bcd
+        st = torch.full((D["B"], D["Hkv"], n_rb, ntl), 255, dtype=torch.uint8, device=dev)
+        mg = torch.empty((D["B"], D["Hkv"], n_rb, ntl), dtype=torch.float32, device=dev)
+        F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=0.0, o=od, workspace=wsd, tile_status=st,
+                             tile_margin=mg)
+        torch.cuda.synchronize()
+        mv = np.sort(mg.cpu().numpy()[st.cpu().numpy() != 2].astype(np.float64))
+        del st, mg
+        curve = []
+        for f_t in (0.1, 0.3, 0.5, 0.7, 0.9):
+            idx = min(int(f_t * len(mv)), len(mv) - 1)
+            la = min(1.0, math.exp(float(mv[idx])) * (1 + 1e-6))  # just above that margin
+            fn = lambda la=la: F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od,  # noqa
+                                                    workspace=wsd, stream=stream)
+            msa = _time_calls(fn, args.steps, args.warmup, stream)
+            cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+            F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od, counters=cnt, workspace=wsd)
+            torch.cuda.synchronize()
+            vis, sk = (int(x) for x in cnt.cpu().tolist())
+            f = sk / max(vis, 1)
+            nbytes = tile_bytes * (2 * vis - sk) + qd.numel() * 2 + od.numel() * 2
+            curve.append({"target_skip": f_t, "lambda": la, "skip_fraction": f, "ms": msa,
+                          "speedup_vs_lambda0": msd0 / msa, "ceiling_2/(2-f)": 2.0 / (2.0 - f),
+                          "GB/s": nbytes / (msa * 1e-3) / 1e9,
+                          "hbm_frac": nbytes / (msa * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        _progress("decode gqa skip curve done")
     if args.part == "all":
         del kd, vd
         q1, k1, v1, kv1 = decode_inputs(B=D["B"], Hq=D["Hq"], Hkv=D["Hkv"], L=D["L"], d_qk=D["d"],
@@ -418,7 +452,7 @@ def _decode_part(F, torch, args, dev, stream, out):
         _progress("decode gqa centre gain 1 done")
     out["decode_gqa"] = {"workload": "GQA decode B64 Hq32/Hkv8 KV32768 d128 bf16, "
                                      f"centre gain {DECODE_BETA}, tile {brd}x{bcd}, {sd} splits",
-                         "points": dec, "paged": paged,
+                         "points": dec, "paged": paged, "skip_curve": curve,
                          "literal_gain1": gain1 if args.part == "all" else None,
                          "traffic_lambda_16/L": _traffic_from_profile(
                              "decode.hip", "decode_gqa_B64_L32768_hbm_counters.json")}
