@@ -493,6 +493,42 @@ def _mla_part(F, torch, args, dev, stream, out):
                     "executed_tflops": flops / (msm * 1e-3) / 1e12,
                     "speedup_vs_lambda0": (msm0 / msm) if msm0 else None})
         _progress(f"decode mla a={a:g}: {msm:.4f} ms")
+    curve = None
+    if msm0 is not None:
+        # Speedup against skip fraction from margin quantiles, as for the other kernels. MLA reads
+        # all of K whatever is skipped (V is K's first 512 columns, already on chip), so a
+        # skipped tile saves P.V matrix work only: the FLOP ceiling is
+        # (576 + 512) / (576 + 512 (1 - f)).
+        import numpy as np
+
+        n_rb = (M["Hq"] + brm - 1) // brm
+        ntl = (M["L"] + bcm - 1) // bcm
+        st = torch.full((M["B"], 1, n_rb, ntl), 255, dtype=torch.uint8, device=dev)
+        mg = torch.empty((M["B"], 1, n_rb, ntl), dtype=torch.float32, device=dev)
+        F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=0.0, o=om, workspace=wsm, tile_status=st,
+                             tile_margin=mg)
+        torch.cuda.synchronize()
+        mv = np.sort(mg.cpu().numpy()[st.cpu().numpy() != 2].astype(np.float64))
+        del st, mg
+        curve = []
+        for f_t in (0.1, 0.3, 0.5, 0.7, 0.9):
+            idx = min(int(f_t * len(mv)), len(mv) - 1)
+            la = min(1.0, math.exp(float(mv[idx])) * (1 + 1e-6))  # just above that margin
+            fn = lambda la=la: F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om,  # noqa
+                                                    workspace=wsm, stream=stream)
+            msa = _time_calls(fn, args.steps, args.warmup, stream)
+            cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+            F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om, counters=cnt, workspace=wsm)
+            torch.cuda.synchronize()
+            vis, sk = (int(x) for x in cnt.cpu().tolist())
+            f = sk / max(vis, 1)
+            flops = 2.0 * brm * bcm * (576 * vis + 512 * (vis - sk))
+            curve.append({"target_skip": f_t, "lambda": la, "skip_fraction": f, "ms": msa,
+                          "speedup_vs_lambda0": msm0 / msa,
+                          "flop_ceiling": (576.0 + 512.0) / (576.0 + 512.0 * (1.0 - f)),
+                          "executed_tflops": flops / (msa * 1e-3) / 1e12,
+                          "hbm_frac": mla_bytes / (msa * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        _progress("decode mla skip curve done")
     gain1 = None
     if args.part == "all":
         del km, vm
@@ -508,7 +544,7 @@ def _mla_part(F, torch, args, dev, stream, out):
         _progress("decode mla centre gain 1 done")
     out["decode_mla"] = {"workload": "MLA-shaped decode B32 Hq128 KV65536 d_qk576/d_v512 bf16, "
                                      f"centre gain {MLA_BETA}, tile {brm}x{bcm}, {sm} splits",
-                         "points": mla, "literal_gain1": gain1,
+                         "points": mla, "skip_curve": curve, "literal_gain1": gain1,
                          "traffic_lambda_16/L": _traffic_from_profile(
                              "mla.hip", "decode_mla_B32_L65536_hbm_counters.json")}
 
