@@ -185,13 +185,13 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     }
   };
 
-  // O^T of this wave's 128 columns for both row groups of the unit: oacc[rb][db] holds columns
-  // 128 wv + 32 db .. + 31 of heads 32 rb .. + 31.
+  // O^T of this wave's 128 columns for both row groups of the unit: oacc[r][db] holds columns
+  // 128 wv + 32 db .. + 31 of heads 32 r .. + 31.
   f32x16_t oacc[2][kDvBlocks];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int db = 0; db < kDvBlocks; ++db) oacc[rb][db] = (f32x16_t)0.f;
+    for (int db = 0; db < kDvBlocks; ++db) oacc[r][db] = (f32x16_t)0.f;
   float m_run = -INFINITY;    // running max of this wave's rows (base 2)
   float m_run_o = -INFINITY;  // running max of the other row group's rows (for the vote)
   float m_ref = -INFINITY, l_part = 0.f;
@@ -286,12 +286,12 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   auto pv = [&](int st) {
     constexpr int NM = 4 * kDvBlocks;  // 16 V^T fragments: (ks, db) = (m / 4, m % 4)
     constexpr int RA = 2;
-    // B operands: P of row group rb, k-step ks, as published by wave rb + 2 (ks / 2).
+    // B operands: P of row group r, k-step ks, as published by wave r + 2 (ks / 2).
     bf16x8_t pb[2][4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) pb[rb][ks] = sP[rb + 2 * (ks >> 1)][ks & 1][lane];
+      for (int ks = 0; ks < 4; ++ks) pb[r][ks] = sP[r + 2 * (ks >> 1)][ks & 1][lane];
     const char *vl = smem[st];
     auto rdv = [&](int m) {
       const int ks = m / kDvBlocks, db = m % kDvBlocks;
@@ -308,9 +308,9 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     for (int m = 0; m < NM; ++m) {
       if (m + RA < NM) va[(m + RA) % (RA + 1)] = rdv(m + RA);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        oacc[rb][m % kDvBlocks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            va[m % (RA + 1)], pb[rb][m / kDvBlocks], oacc[rb][m % kDvBlocks], 0, 0, 0);
+      for (int r = 0; r < 2; ++r)
+        oacc[r][m % kDvBlocks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            va[m % (RA + 1)], pb[r][m / kDvBlocks], oacc[r][m % kDvBlocks], 0, 0, 0);
     }
   };
 
@@ -421,11 +421,11 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   if (hh == 0) sL[wv][n] = l_mine;
   __syncthreads();
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int h = h0 + 32 * rb + n;
-    if (!(h < p.Hq && 32 * rb + n < p.block_r)) continue;
-    const float l_tot = sL[rb][n] + sL[rb + 2][n];
-    const float m_rb = rb == rg ? m_ref : m_ref_o;
+  for (int r = 0; r < 2; ++r) {
+    const int h = h0 + 32 * r + n;
+    if (!(h < p.Hq && 32 * r + n < p.block_r)) continue;
+    const float l_tot = sL[r][n] + sL[r + 2][n];
+    const float m_r = r == rg ? m_ref : m_ref_o;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (p.num_splits == 1) {
       __bf16 *orow = (__bf16 *)p.o + b * p.o_sb + (int64_t)h * p.o_sh + 128 * wv;
@@ -435,14 +435,14 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
         for (int ig = 0; ig < 4; ++ig) {
           const int d0 = db * 32 + 8 * ig + 4 * hh;
           typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-          const f32x16_t &oa = oacc[rb][db];
+          const f32x16_t &oa = oacc[r][db];
           bf16x4_t ov = {(__bf16)(oa[4 * ig + 0] * inv), (__bf16)(oa[4 * ig + 1] * inv),
                          (__bf16)(oa[4 * ig + 2] * inv), (__bf16)(oa[4 * ig + 3] * inv)};
           *(bf16x4_t *)(orow + d0) = ov;
         }
       }
       if (p.lse && hh == 0 && wv == 0)
-        p.lse[(int64_t)b * p.Hq + h] = l_tot > 0.f ? (m_rb + __log2f(l_tot)) * kLn2 : -INFINITY;
+        p.lse[(int64_t)b * p.Hq + h] = l_tot > 0.f ? (m_r + __log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
       const int64_t row = ((int64_t)b * p.Hq + h) * p.num_splits + split;
       float *op = p.o_part + row * kDv + 128 * wv;
@@ -451,12 +451,12 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig) {
           const int d0 = db * 32 + 8 * ig + 4 * hh;
-          const f32x16_t &oa = oacc[rb][db];
+          const f32x16_t &oa = oacc[r][db];
           *(float4 *)(op + d0) = make_float4(oa[4 * ig + 0] * inv, oa[4 * ig + 1] * inv,
                                              oa[4 * ig + 2] * inv, oa[4 * ig + 3] * inv);
         }
       }
-      if (hh == 0 && wv == 0) p.lse_part[row] = l_tot > 0.f ? m_rb + __log2f(l_tot) : -INFINITY;
+      if (hh == 0 && wv == 0) p.lse_part[row] = l_tot > 0.f ? m_r + __log2f(l_tot) : -INFINITY;
     }
   }
   if (bookkeeper) {
