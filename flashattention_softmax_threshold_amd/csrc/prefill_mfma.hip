@@ -471,10 +471,10 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
       atomicAdd(&p.counters[1], (unsigned long long)skipped);
     }
     if (p.tile_status || p.tile_margin) {
-      for (int j = 0; j < p.n_kvtiles; ++j) {
-        if (j >= j0 && j < n_tiles) continue;
-        if (p.tile_status) p.tile_status[unit_tiles + j] = 2;
-        if (p.tile_margin) p.tile_margin[unit_tiles + j] = -INFINITY;
+      for (int jt = 0; jt < p.n_kvtiles; ++jt) {
+        if (jt >= j0 && jt < n_tiles) continue;
+        if (p.tile_status) p.tile_status[unit_tiles + jt] = 2;
+        if (p.tile_margin) p.tile_margin[unit_tiles + jt] = -INFINITY;
       }
     }
   }
