@@ -1,5 +1,4 @@
 """GPU parity of blasst_attn_prefill against the fp64 oracle, element by element."""
-import math
 import random
 
 import numpy as np

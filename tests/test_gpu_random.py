@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from flashattention_softmax_threshold_amd.inputs import decode_inputs, paged_layout, prefill_inputs
+from flashattention_softmax_threshold_amd.inputs import decode_inputs, paged_layout
 
 from parity import need_gpu, oracle_scale
 import test_gpu_decode as dec
