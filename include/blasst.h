@@ -21,6 +21,9 @@
  *   - Device pointers are HIP device memory owned by the caller; the library allocates nothing
  *     and keeps no state between calls. Launches are asynchronous on `stream` (a hipStream_t;
  *     NULL = the null stream). Kernel faults surface at the caller's next synchronisation.
+ *   - A call issues nothing but kernel launches on `stream` (no allocation, memset, copy or
+ *     host synchronisation), so it may be captured into a HIP graph; a replay reads the buffers'
+ *     contents at replay time and, like an eager call, adds to `counters`.
  *   - Argument checks happen on the host before any launch; a failed check launches nothing and
  *     returns BLASST_ERR_INVALID_ARG or BLASST_ERR_UNSUPPORTED. A failed launch returns
  *     BLASST_ERR_HIP.
