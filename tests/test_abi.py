@@ -296,3 +296,32 @@ def test_generator_sinks_on_a_sequence_shorter_than_the_sink_count():
                              seed=11, beta=4.0, sinks=8)
     assert torch.equal(k[:, :8], k[:, :1].expand(1, 8, 1, 16))
     assert not torch.equal(k[:, 8], k[:, 0])
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; a request for more exits with a message before any GPU
+    work."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
+
+
+def test_unloadable_library_raises_instead_of_falling_back(tmp_path):
+    """The binding has no other path: a library file that does not load is an error."""
+    bogus = tmp_path / "libblasst.so"
+    bogus.write_text("not a shared library")
+    saved_path, saved_lib = F.LIB_PATH, F._lib
+    try:
+        F.LIB_PATH, F._lib = str(bogus), None
+        with pytest.raises(OSError):
+            F.load_library()
+        q = torch.zeros((1, 4, 1, 64), dtype=torch.bfloat16)
+        with pytest.raises((OSError, TypeError, ValueError)):
+            F.blasst_attn_prefill(q, q, q)
+    finally:
+        F.LIB_PATH, F._lib = saved_path, saved_lib
