@@ -7,7 +7,8 @@
 // test says (prefill is not bandwidth-bound and a predictable prefetch beats a conditional one);
 // the exp / rescale / P.V MFMA work is what a skipped tile saves.
 //
-// Data path (one workgroup = 4 waves = one unit of 128 query rows; a wave owns 32 rows):
+// Data path (one unit = 4 waves = 128 query rows, a wave owns 32 rows; a workgroup runs one unit,
+// or two that share every K and V tile):
 //   * K and V tiles (64 keys x D, bf16) go from HBM/L2 straight into LDS with
 //     global_load_lds_dwordx4 (no registers, no LDS store instructions), two stages deep: the
 //     next tile is in flight while the current one is used.
@@ -21,8 +22,8 @@
 //     from the row-major V tile with ds_read_b64_tr_b16 (two per MFMA), whose 16-lane transpose
 //     hands each lane the 8 keys of one column in the accumulator's key order.
 //   * Skip vote: each row votes keep iff it is valid, sees a key of the tile and its margin is
-//     not below tau; a wave ballots, the 4 waves meet through LDS and a barrier, and the branch
-//     is uniform over the workgroup.
+//     not below tau; a wave ballots, the unit's 4 waves meet through LDS and a barrier, and the
+//     branch is uniform over the unit.
 // Block order: units of one KV head are numbered (query block longest-first, then query head),
 // and blocks are dealt to the 8 XCDs so each XCD works through contiguous runs of units: the
 // query heads that share K/V read it through the same L2 at about the same time.
