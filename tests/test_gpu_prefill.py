@@ -109,7 +109,7 @@ def test_tiny_fp32_mha_all_lambdas():
 ])
 def test_cross_length_non_causal(dtype, D, block_r, lq, lkv):
     """Non-causal prefill with Lq != Lkv (cross attention), including a key range shorter than
-    one query block; q, k and v are row slices of longer tensors (strided views)."""
+    one query block (q, k and v are the leading rows of longer generated tensors)."""
     need_gpu()
     B, Hq, Hkv = 2, 8, 2
     q, k, v = prefill_inputs(B=B, L=max(lq, lkv), Hq=Hq, Hkv=Hkv, d=D, cluster_len=64,
@@ -128,6 +128,44 @@ def test_cross_length_non_causal(dtype, D, block_r, lq, lkv):
         assert abs(res["counters"][1] - ref.skipped) <= band_mism
         skipped += ref.skipped
     assert skipped > 0
+
+
+@pytest.mark.parametrize("dtype,D,causal,Hq,Hkv", [
+    (torch.bfloat16, 128, True, 8, 2),
+    (torch.bfloat16, 128, False, 3, 1),
+    (torch.bfloat16, 64, True, 4, 4),
+    (torch.float32, 64, False, 4, 2),
+])
+def test_packed_qkv_and_heads_major_layouts_equal_contiguous_bitwise(dtype, D, causal, Hq, Hkv):
+    """The kernels address Q, K, V and O through their batch, row and head strides only: q, k
+    and v sliced out of one packed [B, L, Hq + 2 Hkv, D] projection, K and V stored heads-major
+    ([B, H, L, D] storage) and O written heads-major give the same bits as contiguous tensors."""
+    need_gpu()
+    B, L = 2, 333
+    q, k, v = prefill_inputs(B=B, L=L, Hq=Hq, Hkv=Hkv, d=D, cluster_len=64, dtype=dtype,
+                             device="cuda", seed=5600 + D + Hq, beta=16.0, sinks=8)
+    packed = torch.cat([q, k, v], dim=2)
+    qp, kp, vp = packed[:, :, :Hq], packed[:, :, Hq:Hq + Hkv], packed[:, :, Hq + Hkv:]
+    kh = k.transpose(1, 2).contiguous().transpose(1, 2)
+    vh = v.transpose(1, 2).contiguous().transpose(1, 2)
+    assert not qp.is_contiguous() and (Hkv == 1 or not kh.is_contiguous())
+    lam = 16.0 / L
+
+    def run(qq, kk, vv, o):
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+        cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+        F.blasst_attn_prefill(qq, kk, vv, causal=causal, lam=lam, o=o, lse=lse, counters=cnt)
+        torch.cuda.synchronize()
+        return o, lse, cnt
+
+    ref = run(q, k, v, torch.empty_like(q))
+    o_heads_major = torch.empty((B, Hq, L, D), dtype=dtype, device="cuda").transpose(1, 2)
+    for name, args in (("packed qkv", (qp, kp, vp, torch.empty_like(q))),
+                       ("heads-major k/v and o", (q, kh, vh, o_heads_major))):
+        print(f"layout {name} {dtype} d{D} causal={causal} Hq{Hq} Hkv{Hkv}", flush=True)
+        got = run(*args)
+        for what, a_, b_ in zip(("o", "lse", "counters"), ref, got):
+            assert torch.equal(a_, b_), f"{name}: {what} differs from the contiguous call"
 
 
 @pytest.mark.parametrize("block_r", [128, 64, 32])
