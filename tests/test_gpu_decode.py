@@ -152,6 +152,43 @@ def test_gqa_decode_full_size_sampled():
         assert ref.skipped > 0
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,splits", [(32, 8, 128, 0), (16, 2, 64, 3), (4, 4, 128, 1)])
+def test_layouts_equal_heads_major_bitwise(Hq, Hkv, D, splits):
+    """The decode kernels address Q, K, V and O through their strides only: K and V stored
+    token-major ([B, L, Hkv, D] contiguous), the query sliced from a packed [B, Hq + 2 Hkv, D]
+    projection and O written into a wider buffer give the same bits as the heads-major cache."""
+    need_gpu()
+    B, L = 3, 1500
+    q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=Hkv, L=L, d_qk=D, d_v=D, cluster_len=64,
+                                 dtype=torch.bfloat16, seed=3500 + Hq + D, beta=16.0, share=True,
+                                 kv_len=[1500, 999, 64])
+    qd, kvd = q.cuda(), kvl.cuda()
+    kh = k.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    vh = v.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    kt, vt = kh.contiguous(), vh.contiguous()
+    packed = torch.cat([qd, torch.zeros((B, 2 * Hkv, D), dtype=qd.dtype, device="cuda")], dim=1)
+    qp = packed[:, :Hq]
+    o_wide = torch.full((B, Hq, D + 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    lam = 16.0 / L
+
+    def run(qq, kk, vv, o):
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+        F.blasst_attn_decode(qq, kk, vv, kv_len=kvd, lam=lam, o=o, lse=lse, counters=cnt,
+                             num_splits=splits)
+        torch.cuda.synchronize()
+        return o, lse, cnt
+
+    ref = run(qd, kh, vh, torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda"))
+    assert not kh.is_contiguous() and kt.is_contiguous() and not qp.is_contiguous()
+    got = run(qp, kt, vt, o_wide[:, :, :D])
+    print(f"decode layouts Hq{Hq} Hkv{Hkv} d{D} splits {splits}: counters {ref[2].tolist()}",
+          flush=True)
+    for what, a_, b_ in zip(("o", "lse", "counters"), ref, got):
+        assert torch.equal(a_, b_), f"{what} differs from the heads-major call"
+    assert torch.all(o_wide[:, :, D:] == 3.0), "columns past d_v were written"
+
+
 def test_mla_small_lengths_and_splits():
     """MLA shape: 128 query heads on one latent KV head, d_qk 576, V = the first 512 columns."""
     L = 700
