@@ -168,6 +168,56 @@ def test_packed_qkv_and_heads_major_layouts_equal_contiguous_bitwise(dtype, D, c
             assert torch.equal(a_, b_), f"{name}: {what} differs from the contiguous call"
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp32_four_wave_query_blocks(causal):
+    """fp32 with B_r = 128 (the generic kernel with four waves per workgroup) on ragged lengths."""
+    need_gpu()
+    L, D = 300, 64
+    q, k, v = prefill_inputs(B=2, L=L, Hq=4, Hkv=2, d=D, cluster_len=64, dtype=torch.float32,
+                             seed=5700 + causal, beta=16.0, sinks=8)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for lam in (0.0, 16 / L, 0.3):
+        what = f"fp32 B_r 128 causal={causal} lam={lam}"
+        print(what, flush=True)
+        res = _run_gpu(qd, kd, vd, causal=causal, lam=lam, block_r=128)
+        assert res["br"] == 128
+        ref = oracle.prefill(q, k, v, causal=causal, block_r=128, block_c=res["bc"],
+                             scale=oracle_scale(D), lam=lam, threads=8)
+        _, band_mism, _ = _check_units(res, ref, q, k, v, causal, lam, what)
+        assert res["counters"][0] == ref.visited
+        assert abs(res["counters"][1] - ref.skipped) <= band_mism
+
+
+def test_bf16_row_stride_beyond_32_bit_tile_offsets():
+    """A K row stride of 2^25 elements puts 64 rows of a tile past a 32-bit byte offset, which
+    the B_r = 128 MFMA kernel keeps per lane; such a call runs on the generic kernel (64-bit
+    addresses) and still matches the oracle. The K storage spans about 9 GB."""
+    need_gpu()
+    B, L, Hq, Hkv, D = 1, 130, 2, 1, 64
+    S = 1 << 25
+    q, k, v = prefill_inputs(B=B, L=L, Hq=Hq, Hkv=Hkv, d=D, cluster_len=32, dtype=torch.bfloat16,
+                             seed=5800, beta=16.0, sinks=4)
+    big = torch.empty(((L - 1) * S + D,), dtype=torch.bfloat16, device="cuda")
+    kd = big.as_strided((B, L, Hkv, D), (L * S, S, D, 1))
+    kd.copy_(k)
+    qd, vd = q.cuda(), v.cuda()
+    assert kd.stride(1) == S and torch.equal(kd.cpu(), k)
+    try:
+        for causal in (True, False):
+            for lam in (0.0, 16 / L):
+                what = f"bf16 row stride 2^25 causal={causal} lam={lam}"
+                print(what, flush=True)
+                res = _run_gpu(qd, kd, vd, causal=causal, lam=lam)
+                ref = oracle.prefill(q, k, v, causal=causal, block_r=res["br"], block_c=res["bc"],
+                                     scale=oracle_scale(D), lam=lam, threads=8)
+                _, band_mism, _ = _check_units(res, ref, q, k, v, causal, lam, what)
+                assert res["counters"][0] == ref.visited
+                assert abs(res["counters"][1] - ref.skipped) <= band_mism
+    finally:
+        del kd, big
+        torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("block_r", [128, 64, 32])
 def test_bf16_causal_gqa_ragged(block_r):
     L = 700
