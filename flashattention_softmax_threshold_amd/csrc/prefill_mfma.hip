@@ -225,8 +225,10 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
 
   // S^T = K Q^T for the tile in K stage st (always computed: the test needs the scores). The K
   // fragments are read from LDS KPF k-steps ahead of the MFMAs that use them, so LDS latency
-  // hides behind matrix work; the scheduling hints keep that order.
-  auto compute_s = [&](int st, f32x16_t *sacc) {
+  // hides behind matrix work; the scheduling hints keep that order. With vj >= 0 the copies of
+  // V_vj and K_{vj+1} are issued between the MFMAs (after the second and the fourth k-step): a
+  // wave held up issuing them still has MFMAs in flight.
+  auto compute_s = [&](int st, f32x16_t *sacc, int vj = -1) {
     constexpr int NS = D / 16;  // k-steps
     constexpr int KPF = NS < 2 ? NS : 2;
     sacc[0] = (f32x16_t)0.f;
@@ -246,6 +248,8 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s][kb], qf[s], sacc[kb], 0, 0, 0);
+      if (s == 1 && vj >= 0) issue_v(vj, vj & 1);
+      if (s == 3 && vj >= 0 && vj + 1 < n_tiles) issue_k(vj + 1, (vj + 1) & 1);
     }
     // Scheduling: KPF steps of reads first, then (2 MFMAs, 2 reads) pairs, then the tail MFMAs.
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * KPF, 0);
@@ -401,11 +405,16 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
     __builtin_amdgcn_s_waitcnt(0);  // this wave's K_j and V_{j-1} have landed
     __syncthreads();                // ... and every wave's; votes for tile j-1 are visible
     const int4 vt = read_votes(j - 1);
-    if (j + 1 < n_tiles) issue_k(j + 1, (j + 1) & 1);
-    issue_v(j, j & 1);
+    // Copies of K_{j+1} and V_j: with two units per workgroup inside the S MFMAs (0.5 % faster
+    // on causal GQA, 1.5 % on non-causal MHA with query-block pairs); with one unit up front
+    // (inside, that kernel spills).
+    if constexpr (NH == 1) {
+      if (j + 1 < n_tiles) issue_k(j + 1, (j + 1) & 1);
+      issue_v(j, j & 1);
+    }
     const int keep_prev = decision(j - 1, vt);
     const float m_prev = m_run;
-    compute_s(j & 1, cur);
+    compute_s(j & 1, cur, NH == 2 ? j : -1);
     mask_tile(j, cur);
     if (keep_prev) {
       rescale_to(m_prev);
