@@ -294,8 +294,45 @@ def _check_tensor(t, name, ndim, device):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if t.stride(-1) != 1:
+    if t.numel() and t.stride(-1) != 1:
         raise ValueError(f"{name}: last dimension must be contiguous")
+
+
+def _check_out(t, name, shape, dtype, device, contiguous):
+    """An optional output buffer the kernels write through a raw pointer: exact shape, dtype and
+    device, and (when the kernels index it densely) contiguous."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not contiguous and t.numel() and t.stride(-1) != 1:
+        raise ValueError(f"{name}: last dimension must be contiguous")
+
+
+def _check_counters(counters, device):
+    """Two uint64 the kernels add to atomically (int64 storage is accepted: same bytes)."""
+    import torch
+
+    if counters is None:
+        return
+    if counters.dtype not in (torch.int64, getattr(torch, "uint64", torch.int64)):
+        raise TypeError(f"counters must be int64 or uint64, got {counters.dtype}")
+    if counters.numel() != 2 or not counters.is_contiguous():
+        raise ValueError(f"counters must be a contiguous tensor of 2 elements, got "
+                         f"{tuple(counters.shape)}")
+    if counters.device != device:
+        raise ValueError(f"counters is on {counters.device}, expected {device}")
+
+
+def _check_on_gpu(device):
+    if device.type != "cuda":
+        raise ValueError(f"tensors are on {device}; the library runs on a GPU device only")
 
 
 def blasst_attn_prefill(q, k, v, *, causal: bool = False, lam: float = 0.0,
@@ -315,6 +352,21 @@ def blasst_attn_prefill(q, k, v, *, causal: bool = False, lam: float = 0.0,
         _check_tensor(t, name, 4, dev)
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
+    _dtype_code(q)
+    B, Lq, Hq, D = q.shape
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} must have the same shape")
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)} in batch or head dim")
+    _check_out(o, "o", q.shape, q.dtype, dev, contiguous=False)
+    _check_out(lse, "lse", (B, Hq, Lq), torch.float32, dev, contiguous=True)
+    _check_counters(counters, dev)
+    if tile_status is not None or tile_margin is not None:
+        br, bc = blasst_prefill_tiles(q, k, block_r=block_r, block_c=block_c)
+        shape = (B, Hq, -(-Lq // br), -(-k.shape[1] // bc))
+        _check_out(tile_status, "tile_status", shape, torch.uint8, dev, contiguous=True)
+        _check_out(tile_margin, "tile_margin", shape, torch.float32, dev, contiguous=True)
+    _check_on_gpu(dev)
     if o is None:
         o = torch.empty(q.shape, dtype=q.dtype, device=dev)
     a = _prefill_args(q, k, v, o, causal=causal, lam=lam, softmax_scale=softmax_scale, lse=lse,
@@ -361,6 +413,49 @@ def _decode_args(q, k, v, o, *, kv_len, lam, softmax_scale, lse, counters, tile_
     return a
 
 
+def _decode_max_len(k, block_table, max_kv_len):
+    """max_kv_len of a decode call: the given value, else the cache length (contiguous: k's
+    row count; paged: pages_per_seq * page_size)."""
+    if max_kv_len is not None:
+        return int(max_kv_len)
+    if block_table is not None:
+        return int(block_table.shape[1]) * int(k.shape[1])
+    return int(k.shape[1])
+
+
+def _check_decode_inputs(q, k, v, kv_len, block_table):
+    """Shapes the decode kernels index through raw pointers: k and v agree with each other and
+    with q (batch, head dim, KV heads dividing the query heads); kv_len holds one int32 per
+    sequence; a block table has one row per sequence."""
+    import torch
+
+    B, Hq, Dqk = q.shape
+    if tuple(k.shape[:3]) != tuple(v.shape[:3]):
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} differ in their first three "
+                         f"dims")
+    if k.shape[3] != Dqk:
+        raise ValueError(f"k head dim {k.shape[3]} does not match q's {Dqk}")
+    if v.shape[3] > k.shape[3] and v.data_ptr() == k.data_ptr():
+        raise ValueError("v aliasing k cannot be wider than k")
+    if k.shape[2] == 0 or Hq % k.shape[2] != 0:
+        raise ValueError(f"{Hq} query heads are not a multiple of {k.shape[2]} KV heads")
+    if block_table is None:
+        if k.shape[0] != B:
+            raise ValueError(f"k has batch {k.shape[0]}, q has {B}")
+    else:
+        if (block_table.dtype != torch.int32 or block_table.device != q.device
+                or block_table.dim() != 2 or not block_table.is_contiguous()
+                or block_table.shape[0] != B):
+            raise TypeError("block_table must be a contiguous int32 [B, pages_per_seq] on the "
+                            "device")
+    if kv_len is not None:
+        if kv_len.dtype != torch.int32 or kv_len.device != q.device:
+            raise TypeError("kv_len must be int32 on the same device")
+        if kv_len.numel() != B or not kv_len.is_contiguous():
+            raise ValueError(f"kv_len must be a contiguous tensor of {B} elements, got "
+                             f"{tuple(kv_len.shape)}")
+
+
 def blasst_decode_plan(q, k, v, *, block_r: int = 0, block_c: int = 0, num_splits: int = 0,
                        block_table=None, max_kv_len=None, window: int = 0):
     """(block_r, block_c, num_splits) a decode call on these tensors uses."""
@@ -400,14 +495,30 @@ def blasst_attn_decode(q, k, v, *, kv_len=None, lam: float = 0.0, softmax_scale:
     _check_tensor(q, "q", 3, dev)
     _check_tensor(k, "k", 4, dev)
     _check_tensor(v, "v", 4, dev)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    _check_decode_inputs(q, k, v, kv_len, block_table)
+    B, Hq = q.shape[0], q.shape[1]
+    _check_out(o, "o", (B, Hq, v.shape[3]), q.dtype, dev, contiguous=False)
+    _check_out(lse, "lse", (B, Hq), torch.float32, dev, contiguous=True)
+    _check_counters(counters, dev)
+    if tile_status is not None or tile_margin is not None:
+        br, bc, _ = blasst_decode_plan(q, k, v, block_r=block_r, block_c=block_c,
+                                       num_splits=num_splits, block_table=block_table,
+                                       max_kv_len=max_kv_len, window=window)
+        Hkv = k.shape[2]
+        L = _decode_max_len(k, block_table, max_kv_len)
+        shape = (B, Hkv, -(-(Hq // Hkv) // br), -(-L // bc))
+        _check_out(tile_status, "tile_status", shape, torch.uint8, dev, contiguous=True)
+        _check_out(tile_margin, "tile_margin", shape, torch.float32, dev, contiguous=True)
+    if workspace is not None:
+        if workspace.device != dev:
+            raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+    _check_on_gpu(dev)
     if o is None:
         o = torch.empty((q.shape[0], q.shape[1], v.shape[3]), dtype=q.dtype, device=dev)
-    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.device != dev):
-        raise TypeError("kv_len must be int32 on the same device")
-    if block_table is not None and (block_table.dtype != torch.int32 or block_table.device != dev
-                                    or block_table.dim() != 2 or not block_table.is_contiguous()
-                                    or block_table.shape[0] != q.shape[0]):
-        raise TypeError("block_table must be a contiguous int32 [B, pages_per_seq] on the device")
     a = _decode_args(q, k, v, o, kv_len=kv_len, lam=lam, softmax_scale=softmax_scale, lse=lse,
                      counters=counters, tile_status=tile_status, tile_margin=tile_margin,
                      block_r=block_r, block_c=block_c, num_splits=num_splits,

@@ -230,6 +230,8 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
   // wave held up issuing them still has MFMAs in flight.
   auto compute_s = [&](int st, f32x16_t *sacc, int vj = -1) {
     constexpr int NS = D / 16;  // k-steps
+    // The V copy goes out after k-step 1 and the K copy after k-step 3: both need four k-steps.
+    static_assert(NS >= 4, "the in-loop copies need at least four k-steps (D >= 64)");
     constexpr int KPF = NS < 2 ? NS : 2;
     sacc[0] = (f32x16_t)0.f;
     sacc[1] = (f32x16_t)0.f;

@@ -325,3 +325,75 @@ def test_unloadable_library_raises_instead_of_falling_back(tmp_path):
             F.blasst_attn_prefill(q, q, q)
     finally:
         F.LIB_PATH, F._lib = saved_path, saved_lib
+
+
+def _expect(exc, match, fn, *args, **kw):
+    with pytest.raises(exc, match=match):
+        fn(*args, **kw)
+
+
+def test_prefill_binding_checks_every_tensor_before_the_call():
+    """Every buffer the prefill kernels address through a raw pointer is checked for shape,
+    dtype, device and layout in the binding, before the library is called (meta tensors: no
+    memory, no GPU). A call whose tensors all pass reaches the last check, the GPU device."""
+    B, L, Hq, Hkv, D = 2, 300, 8, 2, 128
+    q, k, v = _meta((B, L, Hq, D)), _meta((B, L, Hkv, D)), _meta((B, L, Hkv, D))
+    nqb, nkt = -(-L // 128), -(-L // 64)
+    ok = dict(o=_meta((B, L, Hq, D)), lse=_meta((B, Hq, L), torch.float32),
+              counters=_meta((2,), torch.int64),
+              tile_status=_meta((B, Hq, nqb, nkt), torch.uint8),
+              tile_margin=_meta((B, Hq, nqb, nkt), torch.float32))
+    _expect(ValueError, "GPU device", F.blasst_attn_prefill, q, k, v, causal=True, **ok)
+    bad = [
+        (ValueError, "same shape", (q, k, _meta((B, L, Hkv, 64))), {}),
+        (ValueError, "batch or head dim", (q, _meta((1, L, Hkv, D)), _meta((1, L, Hkv, D))), {}),
+        (TypeError, "share a dtype", (q, k, _meta((B, L, Hkv, D), torch.float32)), {}),
+        (ValueError, "o must have shape", (q, k, v), dict(o=_meta((B, L, Hq, 64)))),
+        (TypeError, "o must be", (q, k, v), dict(o=_meta((B, L, Hq, D), torch.float32))),
+        (ValueError, "lse must have shape", (q, k, v), dict(lse=_meta((B, L, Hq), torch.float32))),
+        (TypeError, "lse must be", (q, k, v), dict(lse=_meta((B, Hq, L)))),
+        (ValueError, "lse must be contiguous", (q, k, v),
+         dict(lse=_meta((B, L, Hq), torch.float32).transpose(1, 2))),
+        (TypeError, "counters must be", (q, k, v), dict(counters=_meta((2,), torch.int32))),
+        (ValueError, "2 elements", (q, k, v), dict(counters=_meta((3,), torch.int64))),
+        (ValueError, "tile_status must have shape", (q, k, v),
+         dict(tile_status=_meta((B, Hq, nqb, nkt + 1), torch.uint8))),
+        (TypeError, "tile_margin must be", (q, k, v),
+         dict(tile_margin=_meta((B, Hq, nqb, nkt), torch.float64))),
+        (ValueError, "is on", (q, k, v), dict(counters=torch.zeros(2, dtype=torch.int64))),
+    ]
+    for exc, match, args, kw in bad:
+        _expect(exc, match, F.blasst_attn_prefill, *args, causal=True, **kw)
+
+
+def test_decode_binding_checks_every_tensor_before_the_call():
+    """The same for decode: k / v / q agreement, kv_len, output, LSE, counters, tile arrays,
+    block table and workspace."""
+    B, Hq, Hkv, L, D = 3, 32, 8, 1000, 128
+    q, k, v = _meta((B, Hq, D)), _meta((B, L, Hkv, D)), _meta((B, L, Hkv, D))
+    kvl = _meta((B,), torch.int32)
+    br, bc, _ = F.blasst_decode_plan(q, k, v)
+    st = (B, Hkv, -(-(Hq // Hkv) // br), -(-L // bc))
+    ok = dict(kv_len=kvl, o=_meta((B, Hq, D)), lse=_meta((B, Hq), torch.float32),
+              counters=_meta((2,), torch.int64), tile_status=_meta(st, torch.uint8),
+              tile_margin=_meta(st, torch.float32), workspace=_meta((1 << 20,), torch.uint8))
+    _expect(ValueError, "GPU device", F.blasst_attn_decode, q, k, v, **ok)
+    bad = [
+        (ValueError, "differ in their first three", (q, k, _meta((B, L + 1, Hkv, D))), {}),
+        (ValueError, "head dim", (q, _meta((B, L, Hkv, 64)), _meta((B, L, Hkv, 64))), {}),
+        (ValueError, "not a multiple", (q, _meta((B, L, 3, D)), _meta((B, L, 3, D))), {}),
+        (ValueError, "batch", (q, _meta((B - 1, L, Hkv, D)), _meta((B - 1, L, Hkv, D))), {}),
+        (ValueError, "3 elements", (q, k, v), dict(kv_len=_meta((B - 1,), torch.int32))),
+        (TypeError, "kv_len must be int32", (q, k, v), dict(kv_len=_meta((B,), torch.int64))),
+        (ValueError, "o must have shape", (q, k, v), dict(o=_meta((B, Hq, 64)))),
+        (ValueError, "lse must have shape", (q, k, v), dict(lse=_meta((B, Hq + 1), torch.float32))),
+        (TypeError, "counters must be", (q, k, v), dict(counters=_meta((2,), torch.float32))),
+        (ValueError, "tile_status must have shape", (q, k, v),
+         dict(tile_status=_meta((B, Hkv, 1, 15), torch.uint8))),
+        (TypeError, "block_table", (q, _meta((64, 16, Hkv, D)), _meta((64, 16, Hkv, D))),
+         dict(block_table=_meta((B, 63), torch.int64))),
+        (ValueError, "workspace must be contiguous", (q, k, v),
+         dict(workspace=_meta((64, 64), torch.uint8).t())),
+    ]
+    for exc, match, args, kw in bad:
+        _expect(exc, match, F.blasst_attn_decode, *args, **kw)
