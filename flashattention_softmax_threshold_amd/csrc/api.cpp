@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "blasst.h"
 #include "internal.h"
@@ -34,6 +35,17 @@ bool strides_ok(const int64_t *st, int n, int64_t mult) {
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// The integer a caller stored in an enum field of an argument struct. Callers in C (or through
+// an FFI) may store any int there; reading such a value through the C++ enum type is undefined,
+// so the bytes are read as an int and compared against the named values.
+template <typename E>
+int32_t enum_int(const E &e) {
+  static_assert(sizeof(E) == sizeof(int32_t), "enum fields are 32-bit");
+  int32_t v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 }  // namespace
 
 extern "C" {
@@ -57,7 +69,7 @@ const char *blasst_status_string(blasst_status status) {
 blasst_status blasst_resolve_lambda(const blasst_lambda_spec *spec, int64_t max_kv_len,
                                     double *lambda_out) {
   if (!spec || !lambda_out) return BLASST_ERR_INVALID_ARG;
-  switch (spec->mode) {
+  switch (enum_int(spec->mode)) {
     case BLASST_DENSE:
       *lambda_out = 0.0;
       return BLASST_OK;
@@ -168,8 +180,9 @@ blasst_status blasst_timestep_gate(double disabled_until_timestep, int32_t has_t
 blasst_status blasst_prefill_tiles(const blasst_prefill_args *a, int32_t *block_r,
                                    int32_t *block_c) {
   if (!a || !block_r || !block_c) return BLASST_ERR_INVALID_ARG;
-  if (a->dtype != BLASST_BF16 && a->dtype != BLASST_F32) return BLASST_ERR_UNSUPPORTED;
-  const int br = a->block_r ? a->block_r : (a->dtype == BLASST_BF16 ? 128 : 64);
+  const int32_t dtype = enum_int(a->dtype);
+  if (dtype != BLASST_BF16 && dtype != BLASST_F32) return BLASST_ERR_UNSUPPORTED;
+  const int br = a->block_r ? a->block_r : (dtype == BLASST_BF16 ? 128 : 64);
   const int bc = a->block_c ? a->block_c : blasst::kBlockC;
   if (br != 32 && br != 64 && br != 128) return BLASST_ERR_UNSUPPORTED;
   if (bc != blasst::kBlockC) return BLASST_ERR_UNSUPPORTED;
@@ -180,7 +193,8 @@ blasst_status blasst_prefill_tiles(const blasst_prefill_args *a, int32_t *block_
 
 blasst_status blasst_attn_prefill(const blasst_prefill_args *a, void *stream) {
   if (!a) return BLASST_ERR_INVALID_ARG;
-  if (a->dtype != BLASST_BF16 && a->dtype != BLASST_F32) return BLASST_ERR_UNSUPPORTED;
+  const int32_t dtype = enum_int(a->dtype);
+  if (dtype != BLASST_BF16 && dtype != BLASST_F32) return BLASST_ERR_UNSUPPORTED;
   if (a->batch < 0 || a->len_q < 0 || a->len_kv < 0 || a->heads_q <= 0 || a->heads_kv <= 0)
     return BLASST_ERR_INVALID_ARG;
   if (a->heads_q % a->heads_kv != 0) return BLASST_ERR_INVALID_ARG;
@@ -198,7 +212,7 @@ blasst_status blasst_attn_prefill(const blasst_prefill_args *a, void *stream) {
   if (!a->q || !a->k || !a->v || !a->o) return BLASST_ERR_INVALID_ARG;
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
     return BLASST_ERR_INVALID_ARG;
-  const int64_t mult = a->dtype == BLASST_BF16 ? 8 : 4;
+  const int64_t mult = dtype == BLASST_BF16 ? 8 : 4;
   if (!strides_ok(a->q_stride, 3, mult) || !strides_ok(a->k_stride, 3, mult) ||
       !strides_ok(a->v_stride, 3, mult) || !strides_ok(a->o_stride, 3, mult))
     return BLASST_ERR_INVALID_ARG;
@@ -223,7 +237,7 @@ blasst_status blasst_attn_prefill(const blasst_prefill_args *a, void *stream) {
   p.tile_margin = a->tile_margin;
   p.window = a->window;
   const hipError_t err =
-      blasst::launch_prefill(p, a->dtype == BLASST_BF16 ? 1 : 0, a->head_dim, br,
+      blasst::launch_prefill(p, dtype == BLASST_BF16 ? 1 : 0, a->head_dim, br,
                              (hipStream_t)stream);
   return err == hipSuccess ? BLASST_OK : BLASST_ERR_HIP;
 }
@@ -236,7 +250,7 @@ namespace {
 enum DecodeKind { kNone = 0, kGqa = 1, kMla = 2 };
 
 DecodeKind decode_kind(const blasst_decode_args *a) {
-  if (a->dtype != BLASST_BF16) return kNone;
+  if (enum_int(a->dtype) != BLASST_BF16) return kNone;
   if (a->head_dim_qk == a->head_dim_v && (a->head_dim_qk == 128 || a->head_dim_qk == 64))
     return kGqa;
   if (a->head_dim_qk == 576 && a->head_dim_v == 512 && a->heads_kv == 1 && a->v == a->k)
