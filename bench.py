@@ -1,22 +1,27 @@
 """Benchmark of the BLASST skip-softmax attention forward pass on one MI355X.
 
-Headline step: one causal GQA prefill call (batch 1, 32 query / 8 KV heads, L = 8192, head dim
-128, bf16, tile 128 x 64) at lambda = 16 / L on clustered synthetic inputs whose centre gain puts
-the skip fraction in the pages' 50-75 % range. Printed as ONE JSON line:
+Headline step: one Video-DiT self-attention prefill call -- non-causal MHA, batch 1, 40 heads,
+L = 75600 (21 frames x 3600 tokens), head dim 128, bf16, tile 128 x 64 -- at the threshold the
+Skip-Softmax page's Wan 2.2 calibration gives for target sparsity 0.7:
+lambda = a exp(0.7 b) / L. Inputs are synthetic (frame + 60-token patch clusters). Before the
+first timed call the headline call runs until at least --settle-s seconds of GPU time have
+passed (the clocks settle), then W warm-up calls, then exactly K timed calls between two
+synchronisations. Printed as ONE JSON line:
 
-  value     dense-equivalent TFLOP/s = 4 * Hq * d * L (L + 1) / 2 / (time per call)
+  value     dense-equivalent TFLOP/s = 4 * H * d * L^2 / (time per call)
   roofline  the prefill kernel against the bf16 MFMA peak: executed-tile FLOP per call
             (2 * 128 * 64 * 128 per visited tile for Q K^T, the same per kept tile for P V)
-            / kernel time from HIP events on the launch stream
-  cpu_baseline  the fp64 oracle on a time-bounded random sample of the same call's work units
-            (host cores), in the same unit
+            / the call's time from HIP events on the launch stream (the call is one launch)
+  cpu_baseline  the fp64 oracle on 64 seeded random (query block, head) units of the same call,
+            on the host cores, in the same unit (its full-call time is extrapolated)
 
-Secondary measurements (same line): lambda = 0 on the same kernel and data (speedup), the other
-two thresholds, the literal generator (centre gain 1, nothing skipped), and GQA decode
-(64 x 32/8 heads, KV 32768, d 128) in GB/s against HBM.
+Secondary measurements (same line, each with its own oracle baseline under cpu_baselines):
+lambda = 0 and target sparsity 0.5 of the headline; causal GQA prefill (B1, 32/8 heads, L 8192);
+GQA decode (64 x 32/8 heads, KV 32768) and MLA-shaped decode (32 x 128 heads, KV 65536,
+d 576/512) in GB/s against HBM; the tiny fp32 call; sliding windows; the calibration sweep.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                      [--part all|prefill|decode|mla] [--a A]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-s S] [--no-cpu-baseline]
+                      [--part all|headline|prefill|decode|mla|tiny|window|calib] [--a A]
        python bench.py --copy-calibration BYTES       (reference copy for counter scaling)
        python bench.py --counter-summary ...          (no GPU: rocprofv3 CSV -> profiles/*.json)
 """
@@ -44,6 +49,7 @@ DECODE = dict(B=64, Hq=32, Hkv=8, L=32768, d=128, cluster_len=512, seed=3000)
 DECODE_BETA = 16.0
 MLA = dict(B=32, Hq=128, L=65536, cluster_len=1024, seed=5000)
 MLA_BETA = 16.0
+DIT = dict(L=75600, H=40, d=128, seed=4000, target=0.7)
 DIT_BETA = 4.0  # the Video-DiT generator's centre gain: skip fraction in the pages' range
 WAN_A, WAN_B = 2822.6209952221557, 4.388250623520793  # "Skip-Softmax calibration config"
 PAGE_SIZES = (16, 64)  # paged-cache points of the GQA decode measurement
@@ -54,15 +60,17 @@ CALIB_BETA = 16.0  # smoother score spread than the headline's, so the swept cur
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20, help="timed calls of the headline")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed calls before them")
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="GPU seconds of headline calls before the first timed phase")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--quick", action="store_true", help="same as --part prefill")
-    ap.add_argument("--part", choices=("all", "prefill", "decode", "mla", "calib", "dit",
-                                       "window"),
+    ap.add_argument("--quick", action="store_true", help="same as --part headline")
+    ap.add_argument("--part", choices=("all", "headline", "prefill", "decode", "mla", "tiny",
+                                       "calib", "window"),
                     default="all",
-                    help="prefill: the headline call only; decode / mla: that decode only "
-                         "(profiling runs isolate one kernel this way)")
+                    help="headline: the Video-DiT call only; prefill / decode / mla / tiny: that "
+                         "workload only (profiling runs isolate one kernel this way)")
     ap.add_argument("--a", type=float, default=None,
                     help="decode parts: time only lambda = a / L instead of the sweep")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -77,7 +85,7 @@ def _parse():
     ap.add_argument("--commands", default="", help="with --counter-summary: the commands, recorded")
     args = ap.parse_args()
     if args.quick:
-        args.part = "prefill"
+        args.part = "headline"
     return args
 
 
@@ -86,6 +94,8 @@ def _progress(msg):
 
 
 def _time_calls(fn, steps, warmup, stream):
+    """W untimed calls, then exactly `steps` calls between HIP events on the launch stream,
+    synchronised on both sides. Returns ms per call."""
     import torch
 
     for _ in range(warmup):
@@ -99,6 +109,41 @@ def _time_calls(fn, steps, warmup, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps  # ms per call
+
+
+def _settle(fn, stream, min_s):
+    """Runs fn until at least min_s seconds of GPU time have passed (the clocks reach their
+    loaded state); returns the GPU seconds spent."""
+    import torch
+
+    spent, batch = 0.0, 1
+    while spent < min_s * 1e3:
+        a = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(batch):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        spent += a.elapsed_time(e)
+        batch = min(batch * 2, 64)
+    return spent / 1e3
+
+
+def _time_auto(fn, steps, warmup, stream, min_ms=250.0, max_calls=4000):
+    """Secondary measurements: at least `steps` timed calls and at least min_ms of them (short
+    calls are averaged over more calls), after `warmup` calls and at least 20 ms of settling."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    t0 = _time_calls(fn, 3, 0, stream)
+    n_settle = min(max_calls, int(math.ceil(20.0 / max(t0, 1e-3))))
+    for _ in range(n_settle):
+        fn()
+    n = max(steps, min(max_calls, int(math.ceil(min_ms / max(t0, 1e-3)))))
+    torch.cuda.synchronize()
+    return _time_calls(fn, n, 0, stream)
 
 
 def _prefill_counts(F, q, k, v, lam):
@@ -131,45 +176,78 @@ def _traffic_from_profile(kernel_file, profile_name):
     return rec.get("hbm_bytes_per_launch")
 
 
-def _cpu_baseline(q, k, v, lam, br, bc, budget_s=12.0):
-    """The oracle on a random sample of prefill units, until about budget_s seconds passed."""
+def _oracle_threads():
+    # The host share of a one-GPU machine is 16 CPUs whatever os.cpu_count() reports.
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _cpu_prefill_baseline(q, k, v, *, causal, lam, br, bc, n_sample, seed, label):
+    """The oracle (fp64, OpenMP) on n_sample seeded random (batch, head, query block) units of a
+    prefill call, and one unit on one thread; rates in dense-equivalent TFLOP/s (4 d per visible
+    (row, key) pair) over the sampled units' own work, the full call's time extrapolated by
+    dense-equivalent work."""
     import oracle
 
-    B, L, Hq, d = q.shape
-    n_qb = -(-L // br)
-    units = [(0, h, qb) for h in range(Hq) for qb in range(n_qb)]
-    random.Random(7).shuffle(units)
-    threads = min(16, os.cpu_count() or 1)
+    B, Lq, Hq, d = q.shape
+    Lkv = k.shape[1]
+    n_qb = -(-Lq // br)
+    units = [(b, h, qb) for b in range(B) for h in range(Hq) for qb in range(n_qb)]
+    sample = random.Random(seed).sample(units, min(n_sample, len(units)))
+
+    def dense_flops(us):
+        f = 0.0
+        for (_, _, qb) in us:
+            r0, r1 = qb * br, min((qb + 1) * br, Lq)
+            keys = sum(r + 1 for r in range(r0, r1)) if causal else (r1 - r0) * Lkv
+            f += 4.0 * d * keys
+        return f
+
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
-    done = []
+    threads = _oracle_threads()
     t0 = time.perf_counter()
-    i = 0
-    while i < len(units) and time.perf_counter() - t0 < budget_s:
-        chunk = units[i:i + 64]
-        oracle.prefill(qc, kc, vc, causal=True, block_r=br, block_c=bc, scale=1 / math.sqrt(d),
-                       lam=lam, units=chunk, threads=threads)
-        done += chunk
-        i += 64
-    elapsed = time.perf_counter() - t0
-    # Dense-equivalent FLOP of the sampled units: 4 d per (row, visible key).
-    flops = 0.0
-    for (_, _, qb) in done:
-        r0, r1 = qb * br, min((qb + 1) * br, L)
-        flops += 4.0 * d * sum(r + 1 for r in range(r0, r1))
-    # One thread on a few units, for the per-core rate.
-    one = units[:8]
+    oracle.prefill(qc, kc, vc, causal=causal, block_r=br, block_c=bc, scale=1 / math.sqrt(d),
+                   lam=lam, units=sample, threads=threads)
+    el = time.perf_counter() - t0
     t1 = time.perf_counter()
-    oracle.prefill(qc, kc, vc, causal=True, block_r=br, block_c=bc, scale=1 / math.sqrt(d),
-                   lam=lam, units=one, threads=1)
+    oracle.prefill(qc, kc, vc, causal=causal, block_r=br, block_c=bc, scale=1 / math.sqrt(d),
+                   lam=lam, units=sample[:1], threads=1)
     e1 = time.perf_counter() - t1
-    f1 = sum(4.0 * d * sum(r + 1 for r in range(qb * br, min((qb + 1) * br, L)))
-             for (_, _, qb) in one)
-    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s (dense-equivalent)", cores=threads,
+    f_s, f_all = dense_flops(sample), dense_flops(units)
+    return dict(value=f_s / el / 1e12, unit="TFLOP/s (dense-equivalent)", cores=threads,
                 kind="oracle",
-                sample=f"{len(done)} of {len(units)} causal prefill units (random, seed 7), "
-                       f"{elapsed:.1f} s wall, fp64",
-                value_1_thread=f1 / e1 / 1e12, cpu_model=_cpu_model(),
-                host_cpus=os.cpu_count())
+                sample=f"{len(sample)} of {len(units)} {label} units (seeded random, seed "
+                       f"{seed}), fp64, {el:.1f} s wall; full call extrapolated by work",
+                extrapolated_full_call_s=el * f_all / f_s,
+                value_1_thread=dense_flops(sample[:1]) / e1 / 1e12,
+                cpu_model=_cpu_model(), host_cpus=os.cpu_count())
+
+
+def _cpu_decode_baseline(q, k, v, kvl, *, lam, br, bc, splits, n_sample, seed, label,
+                         tile_bytes_k, tile_bytes_v):
+    """The oracle on n_sample seeded random (sequence, KV head, row block) units of a decode
+    call (all splits of each); rate in GB/s of the units' algorithmic bytes (K of every visited
+    tile, V of every kept tile; an MLA value tile is the key tile, tile_bytes_v = 0)."""
+    import oracle
+
+    B, Hq, dqk = q.shape
+    Hkv = k.shape[2]
+    n_rb = -(-(Hq // Hkv) // br)
+    units = [(b, g, rb) for b in range(B) for g in range(Hkv) for rb in range(n_rb)]
+    sample = random.Random(seed).sample(units, min(n_sample, len(units)))
+    qc, kc, vc, kl = q.cpu(), k.cpu(), v.cpu(), kvl.cpu()
+    threads = _oracle_threads()
+    t0 = time.perf_counter()
+    res = oracle.decode(qc, kc, vc, kv_len=kl, block_r=br, block_c=bc, num_splits=splits,
+                        scale=1 / math.sqrt(dqk), lam=lam, units=sample, threads=threads)
+    el = time.perf_counter() - t0
+    nbytes = sum(tile_bytes_k * u.visited + tile_bytes_v * (u.visited - u.skipped)
+                 for u in res.units.values())
+    return dict(value=nbytes / el / 1e9, unit="GB/s (algorithmic bytes)", cores=threads,
+                kind="oracle",
+                sample=f"{len(sample)} of {len(units)} {label} units (seeded random, seed "
+                       f"{seed}, all {splits} splits each), fp64, {el:.1f} s wall",
+                extrapolated_full_call_s=el * len(units) / len(sample),
+                cpu_model=_cpu_model(), host_cpus=os.cpu_count())
 
 
 def _cpu_model():
@@ -242,6 +320,8 @@ def _write_counter_summary(args):
 
 
 def _prefill_part(F, torch, args, dev, stream, out):
+    """Causal GQA prefill (B1, 32 query / 8 KV heads, L 8192, d 128, tile 128 x 64) at
+    lambda = a / L, a in {4, 16, 64}, beside lambda = 0 on the same kernel and data."""
     from flashattention_softmax_threshold_amd.inputs import prefill_inputs
 
     P = PREFILL
@@ -257,47 +337,27 @@ def _prefill_part(F, torch, args, dev, stream, out):
     def prefill_step(lam, qq=q, kk=k, vv=v):
         return lambda: F.blasst_attn_prefill(qq, kk, vv, causal=True, lam=lam, o=o, stream=stream)
 
-    lam = 16.0 / L
-    ms = _time_calls(prefill_step(lam), args.steps, args.warmup, stream)
-    visited, skipped = _prefill_counts(F, q, k, v, lam)
-    kept = visited - skipped
-    exec_flops = tile_flops * (visited + kept)
-    achieved = exec_flops / (ms * 1e-3) / 1e12
-    _progress(f"prefill headline: {ms:.4f} ms, skip {skipped / visited:.3f}, "
-              f"{achieved:.0f} executed TFLOP/s")
-    traffic = _traffic_from_profile("prefill_mfma.hip", "prefill_mfma_causal_L8192_hbm_counters.json")
-    out.update({
-        "value": dense_flops / (ms * 1e-3) / 1e12,
-        "ms_per_step": ms,
-        "data": f"synthetic clustered (256-token clusters, 64 sink keys, centre gain {PREFILL_BETA})",
-        "config": {"workload": "causal GQA prefill B1 Hq32/Hkv8 L8192 d128 bf16, tile 128x64, "
-                               "lambda=16/L", "batch": 1, "seq_len": L, "heads_q": Hq,
-                   "heads_kv": P["Hkv"], "head_dim": d, "lambda": lam, "tile": [br, bc],
-                   "parallelism": "none (1 GPU)"},
-        "skip_fraction": skipped / visited,
-        "executed_tflops": achieved,
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
-                     "traffic": traffic},
-    })
+    def point(lam, label):
+        ms = _time_auto(prefill_step(lam), args.steps, args.warmup, stream)
+        va, sa = _prefill_counts(F, q, k, v, lam)
+        ex = tile_flops * (2 * va - sa) / (ms * 1e-3) / 1e12
+        return {"lambda": label, "lambda_value": lam, "ms": ms, "skip_fraction": sa / va,
+                "dense_tflops": dense_flops / (ms * 1e-3) / 1e12, "executed_tflops": ex,
+                "mfma_frac": ex / BF16_PEAK_TFLOPS, "ceiling_2/(2-f)": 2.0 / (2.0 - sa / va)}
 
-    if args.part == "all":
-        # Same kernel, same data: lambda = 0 and the other thresholds.
-        ms0 = _time_calls(prefill_step(0.0), args.steps, args.warmup, stream)
-        v0, _ = _prefill_counts(F, q, k, v, 0.0)
-        sweep = []
-        for a in (4.0, 16.0, 64.0):
-            la = a / L
-            msa = ms if a == 16.0 else _time_calls(prefill_step(la), args.steps, args.warmup, stream)
-            va, sa = _prefill_counts(F, q, k, v, la)
-            sweep.append({"lambda": f"{int(a)}/L", "ms": msa, "skip_fraction": sa / va,
-                          "speedup_vs_lambda0": ms0 / msa,
-                          "ceiling_2/(2-f)": 2.0 / (2.0 - sa / va),
-                          "executed_tflops": tile_flops * (2 * va - sa) / (msa * 1e-3) / 1e12})
-        out["prefill_lambda0"] = {"ms": ms0, "dense_tflops": dense_flops / (ms0 * 1e-3) / 1e12,
-                                  "executed_tflops": tile_flops * 2 * v0 / (ms0 * 1e-3) / 1e12}
-        out["prefill_sweep"] = sweep
-        _progress("prefill sweep done")
+    pts = [point(0.0, "0")]
+    for a in (4.0, 16.0, 64.0):
+        pts.append(point(a / L, f"{int(a)}/L"))
+    for pt in pts:
+        pt["speedup_vs_lambda0"] = pts[0]["ms"] / pt["ms"]
+    _progress("prefill causal GQA: " + ", ".join(f"{p_['lambda']} {p_['ms']:.4f} ms"
+                                                 for p_ in pts))
+    res = {"workload": "causal GQA prefill B1 Hq32/Hkv8 L8192 d128 bf16, tile 128x64, "
+                       f"256-token clusters + 64 sink keys, centre gain {PREFILL_BETA}",
+           "points": pts,
+           "traffic_lambda_16/L": _traffic_from_profile(
+               "prefill_mfma.hip", "prefill_mfma_causal_L8192_hbm_counters.json")}
+    if args.part in ("all", "prefill"):
         # Speedup against skip fraction: thresholds at quantiles of the tile margins of one
         # lambda = 0 call (a tile is skipped exactly when its margin is below ln lambda).
         from flashattention_softmax_threshold_amd import calibration as C
@@ -309,34 +369,37 @@ def _prefill_part(F, torch, args, dev, stream, out):
         for f_t in (0.1, 0.3, 0.5, 0.7, 0.9):
             idx = min(int(f_t * len(mv)), len(mv) - 1)
             la = min(1.0, math.exp(float(mv[idx])) * (1 + 1e-6))  # just above that margin
-            msa = _time_calls(prefill_step(la), args.steps, args.warmup, stream)
-            va, sa = _prefill_counts(F, q, k, v, la)
-            curve.append({"target_skip": f_t, "lambda": la, "skip_fraction": sa / va, "ms": msa,
-                          "speedup_vs_lambda0": ms0 / msa,
-                          "ceiling_2/(2-f)": 2.0 / (2.0 - sa / va),
-                          "executed_tflops": tile_flops * (2 * va - sa) / (msa * 1e-3) / 1e12})
-        out["prefill_skip_curve"] = curve
+            pt = point(la, f"margin quantile {f_t}")
+            pt["target_skip"] = f_t
+            pt["speedup_vs_lambda0"] = pts[0]["ms"] / pt["ms"]
+            curve.append(pt)
+        res["skip_curve"] = curve
         del margin, status
         _progress("prefill skip curve done")
         # The recipe read literally (centre gain 1): nothing is skipped; overhead of the test.
         q1, k1, v1 = prefill_inputs(B=P["B"], L=L, Hq=Hq, Hkv=P["Hkv"], d=d,
                                     cluster_len=P["cluster_len"], dtype=torch.bfloat16,
                                     device=dev, seed=P["seed"], beta=1.0, sinks=P["sinks"])
-        ms1 = _time_calls(prefill_step(lam, q1, k1, v1), args.steps, args.warmup, stream)
-        ms10 = _time_calls(prefill_step(0.0, q1, k1, v1), args.steps, args.warmup, stream)
+        lam = 16.0 / L
+        ms1 = _time_auto(prefill_step(lam, q1, k1, v1), args.steps, args.warmup, stream)
+        ms10 = _time_auto(prefill_step(0.0, q1, k1, v1), args.steps, args.warmup, stream)
         v1c, s1c = _prefill_counts(F, q1, k1, v1, lam)
-        out["prefill_literal_gain1"] = {"ms": ms1, "ms_lambda0": ms10,
-                                        "skip_fraction": s1c / v1c,
-                                        "speedup_vs_lambda0": ms10 / ms1}
+        res["literal_gain1"] = {"ms": ms1, "ms_lambda0": ms10, "skip_fraction": s1c / v1c,
+                                "speedup_vs_lambda0": ms10 / ms1}
         del q1, k1, v1
         _progress("prefill centre gain 1 done")
-    return q, k, v, lam, br, bc
+    out["prefill_causal_gqa"] = res
+    if not args.no_cpu_baseline:
+        _progress("cpu baseline: causal GQA prefill")
+        out.setdefault("cpu_baselines", {})["prefill_causal_gqa"] = _cpu_prefill_baseline(
+            q, k, v, causal=True, lam=16.0 / L, br=br, bc=bc, n_sample=64, seed=7,
+            label="causal GQA prefill")
 
 
 def _literal_gain1(fn_of_lam, lams, steps, warmup, stream):
     """Times of the same calls on inputs generated at centre gain 1 (the recipe read literally,
     where nothing is skipped): the cost of taking the test when it never fires."""
-    ms = {f"{k}": _time_calls(fn_of_lam(la), steps, warmup, stream) for k, la in lams}
+    ms = {f"{k}": _time_auto(fn_of_lam(la), steps, warmup, stream) for k, la in lams}
     base = ms[lams[0][0]]
     return {"ms": ms, "time_vs_lambda0": {k: v / base for k, v in ms.items()}}
 
@@ -364,7 +427,7 @@ def _decode_part(F, torch, args, dev, stream, out):
         la = a / D["L"]
         fn = lambda la=la: F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od,  # noqa: E731
                                                 workspace=wsd, stream=stream)
-        msd = _time_calls(fn, args.steps, args.warmup, stream)
+        msd = _time_auto(fn, args.steps, args.warmup, stream)
         cnt = torch.zeros(2, dtype=torch.int64, device=dev)
         F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od, counters=cnt, workspace=wsd)
         torch.cuda.synchronize()
@@ -390,7 +453,7 @@ def _decode_part(F, torch, args, dev, stream, out):
         fn = lambda: F.blasst_attn_decode(qd, kp, vp, kv_len=kvl, lam=la, o=od,  # noqa: E731
                                           workspace=wsd, block_table=table, max_kv_len=D["L"],
                                           stream=stream)
-        msp = _time_calls(fn, args.steps, args.warmup, stream)
+        msp = _time_auto(fn, args.steps, args.warmup, stream)
         cnt = torch.zeros(2, dtype=torch.int64, device=dev)
         F.blasst_attn_decode(qd, kp, vp, kv_len=kvl, lam=la, o=od, counters=cnt, workspace=wsd,
                              block_table=table, max_kv_len=D["L"])
@@ -426,7 +489,7 @@ def _decode_part(F, torch, args, dev, stream, out):
             la = min(1.0, math.exp(float(mv[idx])) * (1 + 1e-6))  # just above that margin
             fn = lambda la=la: F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od,  # noqa
                                                     workspace=wsd, stream=stream)
-            msa = _time_calls(fn, args.steps, args.warmup, stream)
+            msa = _time_auto(fn, args.steps, args.warmup, stream)
             cnt = torch.zeros(2, dtype=torch.int64, device=dev)
             F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=la, o=od, counters=cnt, workspace=wsd)
             torch.cuda.synchronize()
@@ -450,6 +513,18 @@ def _decode_part(F, torch, args, dev, stream, out):
             [("0", 0.0), ("16/L", 16.0 / D["L"])], args.steps, args.warmup, stream)
         del q1, k1, v1
         _progress("decode gqa centre gain 1 done")
+    if not args.no_cpu_baseline and args.part in ("all", "decode"):
+        _progress("cpu baseline: GQA decode")
+        if args.part == "all":  # K and V were freed for the centre-gain-1 inputs: regenerate
+            qd, kd, vd, kvl = decode_inputs(B=D["B"], Hq=D["Hq"], Hkv=D["Hkv"], L=D["L"],
+                                            d_qk=D["d"], d_v=D["d"], cluster_len=D["cluster_len"],
+                                            dtype=torch.bfloat16, device=dev, seed=D["seed"],
+                                            beta=DECODE_BETA)
+        out.setdefault("cpu_baselines", {})["decode_gqa"] = _cpu_decode_baseline(
+            qd, kd, vd, kvl, lam=16.0 / D["L"], br=brd, bc=bcd, splits=sd, n_sample=64, seed=5,
+            label="GQA decode (sequence, KV head)", tile_bytes_k=tile_bytes,
+            tile_bytes_v=tile_bytes)
+        del qd, kd, vd
     out["decode_gqa"] = {"workload": "GQA decode B64 Hq32/Hkv8 KV32768 d128 bf16, "
                                      f"centre gain {DECODE_BETA}, tile {brd}x{bcd}, {sd} splits",
                          "points": dec, "paged": paged, "skip_curve": curve,
@@ -478,7 +553,7 @@ def _mla_part(F, torch, args, dev, stream, out):
         la = a / M["L"]
         fn = lambda la=la: F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om,  # noqa: E731
                                                 workspace=wsm, stream=stream)
-        msm = _time_calls(fn, args.steps, args.warmup, stream)
+        msm = _time_auto(fn, args.steps, args.warmup, stream)
         cnt = torch.zeros(2, dtype=torch.int64, device=dev)
         F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om, counters=cnt, workspace=wsm)
         torch.cuda.synchronize()
@@ -516,7 +591,7 @@ def _mla_part(F, torch, args, dev, stream, out):
             la = min(1.0, math.exp(float(mv[idx])) * (1 + 1e-6))  # just above that margin
             fn = lambda la=la: F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om,  # noqa
                                                     workspace=wsm, stream=stream)
-            msa = _time_calls(fn, args.steps, args.warmup, stream)
+            msa = _time_auto(fn, args.steps, args.warmup, stream)
             cnt = torch.zeros(2, dtype=torch.int64, device=dev)
             F.blasst_attn_decode(qm, km, vm, kv_len=kvm, lam=la, o=om, counters=cnt, workspace=wsm)
             torch.cuda.synchronize()
@@ -542,6 +617,17 @@ def _mla_part(F, torch, args, dev, stream, out):
             [("0", 0.0), ("16/L", 16.0 / M["L"])], args.steps, args.warmup, stream)
         del q1, k1, v1
         _progress("decode mla centre gain 1 done")
+    if not args.no_cpu_baseline and args.part in ("all", "mla"):
+        _progress("cpu baseline: MLA decode")
+        if args.part == "all":
+            qm, km, vm, kvm = decode_inputs(B=M["B"], Hq=M["Hq"], Hkv=1, L=M["L"], d_qk=576,
+                                            d_v=512, cluster_len=M["cluster_len"],
+                                            dtype=torch.bfloat16, device=dev, seed=M["seed"],
+                                            beta=MLA_BETA, share=True, v_aliases_k=True)
+        out.setdefault("cpu_baselines", {})["decode_mla"] = _cpu_decode_baseline(
+            qm, km, vm, kvm, lam=16.0 / M["L"], br=brm, bc=bcm, splits=sm, n_sample=4, seed=5,
+            label="MLA decode (sequence, row block)", tile_bytes_k=bcm * 576 * 2, tile_bytes_v=0)
+        del qm, km, vm
     out["decode_mla"] = {"workload": "MLA-shaped decode B32 Hq128 KV65536 d_qk576/d_v512 bf16, "
                                      f"centre gain {MLA_BETA}, tile {brm}x{bcm}, {sm} splits",
                          "points": mla, "skip_curve": curve, "literal_gain1": gain1,
@@ -549,58 +635,131 @@ def _mla_part(F, torch, args, dev, stream, out):
                              "mla.hip", "decode_mla_B32_L65536_hbm_counters.json")}
 
 
-def _dit_part(F, torch, args, dev, stream, out):
-    """Video-DiT self-attention (non-causal, 40 heads, 21 frames x 3600 tokens, d 128): lambda from
-    a target sparsity through the Wan 2.2 calibration of the Skip-Softmax page."""
+def _headline_part(F, torch, args, dev, stream, out):
+    """Video-DiT self-attention (non-causal, 40 heads, 21 frames x 3600 tokens, d 128): lambda
+    from a target sparsity through the Wan 2.2 calibration of the Skip-Softmax page. The
+    headline is target sparsity 0.7; lambda = 0 and target 0.5 are measured beside it."""
     from flashattention_softmax_threshold_amd.inputs import prefill_inputs
 
-    L, H, d = 75600, 40, 128
+    L, H, d = DIT["L"], DIT["H"], DIT["d"]
     q, k, v = prefill_inputs(B=1, L=L, Hq=H, Hkv=H, d=d, cluster_len=60, dtype=torch.bfloat16,
-                             device=dev, seed=4000, beta=DIT_BETA, frame_len=3600, patch_len=60)
+                             device=dev, seed=DIT["seed"], beta=DIT_BETA, frame_len=3600,
+                             patch_len=60)
     br, bc = F.blasst_prefill_tiles(q, k)
     o = torch.empty_like(q)
     tile_flops = 2.0 * br * bc * d
     dense_flops = 4.0 * H * d * float(L) * L
-    steps, warm = max(args.steps // 10, 3), max(args.warmup // 10, 2)
-    pts = []
-    ms0 = None
-    for s_t in (None, 0.5, 0.7):
-        lam = 0.0 if s_t is None else F.blasst_resolve_lambda(
+
+    def lam_of(s_t):
+        return 0.0 if s_t is None else F.blasst_resolve_lambda(
             F.BLASST_TARGET_SPARSITY, L, target_sparsity=s_t, a=WAN_A, b=WAN_B)
-        ms = _time_calls(lambda: F.blasst_attn_prefill(q, k, v, causal=False, lam=lam, o=o,  # noqa
-                                                       stream=stream), steps, warm, stream)
+
+    def call(lam):
+        return lambda: F.blasst_attn_prefill(q, k, v, causal=False, lam=lam, o=o, stream=stream)
+
+    def counts(lam):
+        cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+        F.blasst_attn_prefill(q, k, v, causal=False, lam=lam, counters=cnt, stream=stream)
+        torch.cuda.synchronize()
+        return tuple(int(x) for x in cnt.cpu().tolist())
+
+    lam = lam_of(DIT["target"])
+    settle_s = _settle(call(lam), stream, args.settle_s)
+    ms = _time_calls(call(lam), args.steps, args.warmup, stream)
+    vis, sk = counts(lam)
+    achieved = tile_flops * (2 * vis - sk) / (ms * 1e-3) / 1e12
+    _progress(f"headline Video-DiT s={DIT['target']}: {ms:.3f} ms, skip {sk / vis:.3f}, "
+              f"{achieved:.0f} executed TFLOP/s (settled {settle_s:.2f} GPU s)")
+    traffic = _traffic_from_profile("prefill_mfma.hip", "prefill_mfma_video_dit_hbm_counters.json")
+    out.update({
+        "value": dense_flops / (ms * 1e-3) / 1e12,
+        "ms_per_step": ms,
+        "settle_s": settle_s,
+        "data": f"synthetic clustered (21 frames x 3600 tokens, frame + 60-token patch centres, "
+                f"centre gain {DIT_BETA})",
+        "config": {"workload": "Video-DiT non-causal self-attention B1 H40 L75600 (21 x 3600) "
+                               "d128 bf16, tile 128x64, lambda = a e^(0.7 b) / L (Wan 2.2 "
+                               "calibration, target sparsity 0.7)",
+                   "batch": 1, "seq_len": L, "heads": H, "head_dim": d, "lambda": lam,
+                   "target_sparsity": DIT["target"], "tile": [br, bc],
+                   "parallelism": "none (1 GPU)"},
+        "skip_fraction": sk / vis,
+        "executed_tflops": achieved,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                     "traffic": traffic},
+    })
+    pts = [{"target_sparsity": DIT["target"], "lambda": lam, "ms": ms, "skip_fraction": sk / vis,
+            "dense_tflops": out["value"], "executed_tflops": achieved,
+            "mfma_frac": achieved / BF16_PEAK_TFLOPS, "ceiling_2/(2-f)": 2.0 / (2.0 - sk / vis)}]
+    if args.part == "all":
+        for s_t in (None, 0.5):
+            la = lam_of(s_t)
+            msx = _time_calls(call(la), args.steps, args.warmup, stream)
+            vx, sx = counts(la)
+            ex = tile_flops * (2 * vx - sx) / (msx * 1e-3) / 1e12
+            pts.append({"target_sparsity": s_t, "lambda": la, "ms": msx, "skip_fraction": sx / vx,
+                        "dense_tflops": dense_flops / (msx * 1e-3) / 1e12, "executed_tflops": ex,
+                        "mfma_frac": ex / BF16_PEAK_TFLOPS,
+                        "ceiling_2/(2-f)": 2.0 / (2.0 - sx / vx)})
+            _progress(f"video dit s={s_t}: {msx:.3f} ms")
+        ms0 = pts[1]["ms"]
+        for pt in pts:
+            pt["speedup_vs_lambda0"] = ms0 / pt["ms"]
+        out["speedup_vs_lambda0"] = ms0 / ms
+    out["video_dit_points"] = pts
+    cpu = None
+    if not args.no_cpu_baseline:
+        _progress("cpu baseline: Video-DiT (64 sampled units)")
+        cpu = _cpu_prefill_baseline(q, k, v, causal=False, lam=lam, br=br, bc=bc, n_sample=64,
+                                    seed=11, label="Video-DiT (query block, head)")
+    if args.part == "all":
+        del q, k, v
+        q1, k1, v1 = prefill_inputs(B=1, L=L, Hq=H, Hkv=H, d=d, cluster_len=60,
+                                    dtype=torch.bfloat16, device=dev, seed=DIT["seed"], beta=1.0,
+                                    frame_len=3600, patch_len=60)
+        lam5 = lam_of(0.5)
+        ms_g = {}
+        for name, la in (("0", 0.0), ("target 0.5", lam5)):
+            ms_g[name] = _time_calls(
+                lambda: F.blasst_attn_prefill(q1, k1, v1, causal=False, lam=la, o=o,  # noqa
+                                              stream=stream), max(args.steps // 4, 3), 2, stream)
+        cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+        F.blasst_attn_prefill(q1, k1, v1, causal=False, lam=lam5, counters=cnt)
+        torch.cuda.synchronize()
+        vis1, sk1 = (int(x) for x in cnt.cpu().tolist())
+        out["video_dit_literal_gain1"] = {"ms": ms_g, "time_vs_lambda0": {
+            kk: vv / ms_g["0"] for kk, vv in ms_g.items()}, "skip_fraction_target_0.5": sk1 / vis1}
+        del q1, k1, v1
+        _progress("video dit centre gain 1 done")
+    return cpu
+
+
+def _tiny_part(F, torch, args, dev, stream, out):
+    """The tiny fp32 call (non-causal MHA B1 H2 L512 d64, tile 64 x 64): launch-bound, for
+    correctness; timed for completeness with its oracle beside it (all 16 units)."""
+    from flashattention_softmax_threshold_amd.inputs import prefill_inputs
+
+    q, k, v = prefill_inputs(B=1, L=512, Hq=2, Hkv=2, d=64, cluster_len=64, dtype=torch.float32,
+                             device=dev, seed=1000, beta=8.0)
+    br, bc = F.blasst_prefill_tiles(q, k)
+    o = torch.empty_like(q)
+    pts = []
+    for lam in (0.0, 1e-3, 1e-2, 1e-1):
+        ms = _time_auto(lambda: F.blasst_attn_prefill(q, k, v, causal=False, lam=lam, o=o,  # noqa
+                                                      stream=stream), args.steps, args.warmup,
+                        stream, min_ms=50.0)
         cnt = torch.zeros(2, dtype=torch.int64, device=dev)
         F.blasst_attn_prefill(q, k, v, causal=False, lam=lam, counters=cnt)
         torch.cuda.synchronize()
         vis, sk = (int(x) for x in cnt.cpu().tolist())
-        if s_t is None:
-            ms0 = ms
-        ex = tile_flops * (2 * vis - sk) / (ms * 1e-3) / 1e12
-        pts.append({"target_sparsity": s_t, "lambda": lam, "ms": ms, "skip_fraction": sk / vis,
-                    "dense_tflops": dense_flops / (ms * 1e-3) / 1e12, "executed_tflops": ex,
-                    "mfma_frac": ex / BF16_PEAK_TFLOPS, "speedup_vs_lambda0": ms0 / ms,
-                    "ceiling_2/(2-f)": 2.0 / (2.0 - sk / vis)})
-        _progress(f"video dit s={s_t}: {ms:.3f} ms")
-    del q, k, v
-    q1, k1, v1 = prefill_inputs(B=1, L=L, Hq=H, Hkv=H, d=d, cluster_len=60, dtype=torch.bfloat16,
-                                device=dev, seed=4000, beta=1.0, frame_len=3600, patch_len=60)
-    lam5 = F.blasst_resolve_lambda(F.BLASST_TARGET_SPARSITY, L, target_sparsity=0.5, a=WAN_A,
-                                   b=WAN_B)
-    gain1 = _literal_gain1(
-        lambda la: (lambda: F.blasst_attn_prefill(q1, k1, v1, causal=False, lam=la, o=o,
-                                                  stream=stream)),
-        [("0", 0.0), ("target 0.5", lam5)], steps, warm, stream)
-    cnt = torch.zeros(2, dtype=torch.int64, device=dev)
-    F.blasst_attn_prefill(q1, k1, v1, causal=False, lam=lam5, counters=cnt)
-    torch.cuda.synchronize()
-    vis1, sk1 = (int(x) for x in cnt.cpu().tolist())
-    gain1["skip_fraction_target_0.5"] = sk1 / vis1
-    del q1, k1, v1
-    _progress("video dit centre gain 1 done")
-    out["prefill_video_dit"] = {"workload": "non-causal MHA B1 H40 L75600 (21 x 3600) d128 bf16, "
-                                            f"tile {br}x{bc}, frame + 60-token patch clusters, "
-                                            f"centre gain {DIT_BETA}", "points": pts,
-                                "literal_gain1": gain1}
+        pts.append({"lambda": lam, "ms": ms, "skip_fraction": sk / vis})
+    out["prefill_tiny_fp32"] = {"workload": "non-causal MHA B1 H2 L512 d64 fp32, tile "
+                                            f"{br}x{bc}, centre gain 8", "points": pts}
+    if not args.no_cpu_baseline:
+        out.setdefault("cpu_baselines", {})["prefill_tiny_fp32"] = _cpu_prefill_baseline(
+            q, k, v, causal=False, lam=1e-2, br=br, bc=bc, n_sample=16, seed=3,
+            label="tiny fp32 (all)")
 
 
 def _window_part(F, torch, args, dev, stream, out):
@@ -622,9 +781,9 @@ def _window_part(F, torch, args, dev, stream, out):
     ms0 = None
     for a in (0.0, 16.0):
         lam = a / W
-        ms = _time_calls(lambda: F.blasst_attn_prefill(q, k, v, causal=True, lam=lam, o=o,  # noqa
-                                                       window=W, stream=stream),
-                         args.steps, args.warmup, stream)
+        ms = _time_auto(lambda: F.blasst_attn_prefill(q, k, v, causal=True, lam=lam, o=o,  # noqa
+                                                      window=W, stream=stream),
+                        args.steps, args.warmup, stream)
         cnt = torch.zeros(2, dtype=torch.int64, device=dev)
         F.blasst_attn_prefill(q, k, v, causal=True, lam=lam, counters=cnt, window=W)
         torch.cuda.synchronize()
@@ -652,9 +811,9 @@ def _window_part(F, torch, args, dev, stream, out):
     dpts = []
     for a in (0.0, 16.0):
         lam = a / Wd
-        ms = _time_calls(lambda: F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=lam, o=od,  # noqa
-                                                      workspace=wsd, window=Wd, stream=stream),
-                         args.steps, args.warmup, stream)
+        ms = _time_auto(lambda: F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=lam, o=od,  # noqa
+                                                     workspace=wsd, window=Wd, stream=stream),
+                        args.steps, args.warmup, stream)
         cnt = torch.zeros(2, dtype=torch.int64, device=dev)
         F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=lam, o=od, counters=cnt, workspace=wsd,
                              window=Wd)
@@ -684,8 +843,8 @@ def _calib_part(F, torch, args, dev, stream, out):
         q, k, v = prefill_inputs(B=P["B"], L=L, Hq=P["Hq"], Hkv=P["Hkv"], d=P["d"],
                                  cluster_len=P["cluster_len"], dtype=torch.bfloat16, device=dev,
                                  seed=P["seed"] + L, beta=CALIB_BETA, sinks=P["sinks"])
-        ms = _time_calls(lambda: C.prefill_margins(q, k, v, causal=True, stream=stream),
-                         max(args.steps // 10, 3), max(args.warmup // 10, 1), stream)
+        ms = _time_auto(lambda: C.prefill_margins(q, k, v, causal=True, stream=stream),
+                        3, 1, stream, min_ms=50.0)
         margin, status = C.prefill_margins(q, k, v, causal=True, stream=stream)
         torch.cuda.synchronize()
         margin, status = margin.cpu(), status.cpu()
@@ -743,23 +902,28 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
     }
-    headline = None
+    cpu = None
+    if args.part in ("all", "headline"):
+        cpu = _headline_part(F, torch, args, dev, stream, out)
+        torch.cuda.empty_cache()
     if args.part in ("all", "prefill"):
-        headline = _prefill_part(F, torch, args, dev, stream, out)
+        _prefill_part(F, torch, args, dev, stream, out)
+        torch.cuda.empty_cache()
     if args.part in ("all", "decode"):
         _decode_part(F, torch, args, dev, stream, out)
+        torch.cuda.empty_cache()
     if args.part in ("all", "mla"):
         _mla_part(F, torch, args, dev, stream, out)
-    if args.part in ("all", "dit"):
-        _dit_part(F, torch, args, dev, stream, out)
+        torch.cuda.empty_cache()
+    if args.part in ("all", "tiny"):
+        _tiny_part(F, torch, args, dev, stream, out)
     if args.part in ("all", "window"):
         _window_part(F, torch, args, dev, stream, out)
+        torch.cuda.empty_cache()
     if args.part in ("all", "calib"):
         _calib_part(F, torch, args, dev, stream, out)
-    if headline is not None and not args.no_cpu_baseline:
-        q, k, v, lam, br, bc = headline
-        _progress("cpu baseline (oracle, about 12 s)")
-        out["cpu_baseline"] = _cpu_baseline(q, k, v, lam, br, bc)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -81,8 +81,15 @@ def assert_lse_close(lse_gpu: np.ndarray, lse_ref: np.ndarray, dtype, what: str)
 
 
 def compare_tile_status(st_gpu: np.ndarray, st_ref: np.ndarray, margin_ref: np.ndarray,
-                        lam: float, what: str, band_width: float = MARGIN_BAND):
-    """Exact agreement outside the margin band; returns (#mismatches inside the band, #band)."""
+                        lam: float, what: str, band_width: float = MARGIN_BAND,
+                        margin_gpu: np.ndarray | None = None, stats: dict | None = None):
+    """Exact agreement outside the margin band; returns (#mismatches inside the band, #band).
+
+    With margin_gpu (the kernel's tile_margin output for the same tiles) the margins themselves
+    must agree to within the band on every tile (the same non-finite tiles, |d margin| <=
+    band_width elsewhere): a kernel whose margins drift from the oracle's by a systematic bias
+    fails here even when the bias only ever flips tiles inside the band. stats (optional) gathers
+    the largest margin difference seen under 'max_dmargin'."""
     st_gpu = np.asarray(st_gpu).ravel()
     st_ref = np.asarray(st_ref).ravel()
     margin_ref = np.asarray(margin_ref).ravel()
@@ -93,6 +100,19 @@ def compare_tile_status(st_gpu: np.ndarray, st_ref: np.ndarray, margin_ref: np.n
     bad = mism & ~band
     assert not bad.any(), f"{what}: {int(bad.sum())} tile decisions differ outside the band " \
                           f"(first at {int(np.argmax(bad))}: gpu {st_gpu[bad][0]} ref {st_ref[bad][0]})"
+    assert int(mism.sum()) <= int(band.sum()), f"{what}: more flips than band tiles"
+    if margin_gpu is not None:
+        mg = np.asarray(margin_gpu, dtype=np.float64).ravel()
+        fin = np.isfinite(margin_ref)
+        assert np.array_equal(np.isfinite(mg), fin), \
+            f"{what}: the kernel's margins are finite on other tiles than the oracle's"
+        if fin.any():
+            dm = np.abs(mg[fin] - margin_ref[fin])
+            assert dm.max() <= band_width, \
+                f"{what}: tile margin differs from the oracle's by {dm.max():.3e} " \
+                f"(> {band_width:.1e}) at tile {int(np.flatnonzero(fin)[np.argmax(dm)])}"
+            if stats is not None:
+                stats["max_dmargin"] = max(stats.get("max_dmargin", 0.0), float(dm.max()))
     return int(mism.sum()), int(band.sum())
 
 

@@ -47,17 +47,20 @@ def _check(res, ref, q, k, v, lam, what, kv_len, window=0):
     band_mism = band = 0
     flipped = {}
     bw = MARGIN_BAND
+    stats = {}
     for (b, g, rb), u in ref.units.items():
         nt = len(u.tile_status)
         st = res["status"][b, g, rb]
         m, n = compare_tile_status(st[:nt], u.tile_status, u.tile_margin, lam,
-                                   f"{what} unit {(b, g, rb)}", bw)
+                                   f"{what} unit {(b, g, rb)}", bw,
+                                   margin_gpu=res["margin"][b, g, rb][:nt], stats=stats)
         band_mism += m
         band += n
         assert np.all(st[nt:] == 2), f"{what}: tiles past kv_len must be 'not visited'"
         if m:
             flipped[(b, g, rb)] = st[:nt].copy()
-    print(f"{what}: {band} tiles in the margin band (+-{bw:.1e}), {band_mism} decided the other way",
+    print(f"{what}: {len(ref.units)} units, {band} tiles in the margin band (+-{bw:.1e}), "
+          f"{band_mism} decided the other way, max |d margin| {stats.get('max_dmargin', 0):.2e}",
           flush=True)
     units = dict(ref.units)
     if flipped:
@@ -136,7 +139,8 @@ def test_gqa_decode_full_size_sampled():
     q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=Hkv, L=L, d_qk=128, d_v=128, cluster_len=512,
                                  dtype=torch.bfloat16, device="cuda", seed=3000, beta=16.0)
     rng = random.Random(3)
-    units = [(0, 0, 0), (63, 7, 0)] + [(rng.randrange(B), rng.randrange(Hkv), 0) for _ in range(6)]
+    units = [(0, 0, 0), (63, 7, 0)] + rng.sample(
+        [(b, g, 0) for b in range(1, 63) for g in range(Hkv)], 62)
     for a in (4, 16, 64):
         lam = a / L
         what = f"C3 lam={a}/L"
@@ -241,7 +245,7 @@ def test_mla_decode_full_size_sampled():
     q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=1, L=L, d_qk=576, d_v=512, cluster_len=1024,
                                  dtype=torch.bfloat16, device="cuda", seed=5000, beta=16.0,
                                  share=True, v_aliases_k=True)
-    units = [(0, 0, 0), (31, 0, 1), (7, 0, 0), (19, 0, 1)]
+    units = None  # all 64 (sequence, row block) units, every split
     for a in (4, 64):
         lam = a / L
         what = f"MLA lam={a}/L"

@@ -41,16 +41,19 @@ def _check_units(res, ref, q, k, v, causal, lam, what, window=0):
     band_mism = band = 0
     flipped = {}
     bw = MARGIN_BAND
+    stats = {}
     for (b, h, qb), u in ref.units.items():
         nt = len(u.tile_status)
         st = res["status"][b, h, qb, :nt]
         m, n = compare_tile_status(st, u.tile_status, u.tile_margin, lam,
-                                   f"{what} unit {(b, h, qb)}", bw)
+                                   f"{what} unit {(b, h, qb)}", bw,
+                                   margin_gpu=res["margin"][b, h, qb, :nt], stats=stats)
         band_mism += m
         band += n
         if m:
             flipped[(b, h, qb)] = st.copy()
-    print(f"{what}: {band} tiles in the margin band (+-{bw:.1e}), {band_mism} decided the other way",
+    print(f"{what}: {len(ref.units)} units, {band} tiles in the margin band (+-{bw:.1e}), "
+          f"{band_mism} decided the other way, max |d margin| {stats.get('max_dmargin', 0):.2e}",
           flush=True)
     units = dict(ref.units)
     if flipped:
@@ -270,8 +273,8 @@ def test_causal_gqa_8k_full_size_sampled(beta):
     q, k, v = prefill_inputs(B=1, L=L, Hq=32, Hkv=8, d=128, cluster_len=256,
                              dtype=torch.bfloat16, device="cuda", seed=2000, beta=beta, sinks=64)
     rng = random.Random(5)
-    units = [(0, 0, 0), (0, 31, 63), (0, 5, 63)] + [(0, rng.randrange(32), rng.randrange(64))
-                                                    for _ in range(9)]
+    units = [(0, 0, 0), (0, 31, 63), (0, 5, 63)] + rng.sample(
+        [(0, h, qb) for h in range(32) for qb in range(64)], 61)
     for a in (4, 16, 64):
         what = f"C2 beta={beta} lam={a}/L"
         print(what, flush=True)
@@ -320,7 +323,9 @@ def test_video_dit_full_size_sampled(beta):
                              dtype=torch.bfloat16, device="cuda", seed=4000, beta=beta,
                              frame_len=3600, patch_len=60)
     a, b = 2822.6209952221557, 4.388250623520793
-    units = [(0, 0, 0), (0, 39, 590), (0, 17, 300), (0, 3, 77)]
+    rng = random.Random(6)
+    units = [(0, 0, 0), (0, 39, 590), (0, 17, 300), (0, 3, 77)] + rng.sample(
+        [(0, h, qb) for h in range(40) for qb in range(591)], 60)
     for s in (0.5, 0.7):
         lam = F.blasst_resolve_lambda(F.BLASST_TARGET_SPARSITY, L, target_sparsity=s, a=a, b=b)
         what = f"C4 beta={beta} s={s} lam={lam:.4f}"

@@ -346,6 +346,33 @@ def test_split_ranges_and_combine():
             np.testing.assert_allclose(p["o"], cf["o"], rtol=1e-10, atol=1e-11)
 
 
+def test_split_ranges_with_a_window_explicit_values():
+    """Split ranges of a windowed decode, worked by hand from the reading taken for windows (the
+    splits cut the at most ceil(W / B_c) + 1 tiles a window of W keys can touch, from the tile
+    holding the first visible key kv_len - W, in equal runs of whole tiles, clipped to the
+    sequence)."""
+    # kv_len 1000, W 300, B_c 64: first key 700 is in tile 10 (key 640); span min(16, 5 + 1) = 6
+    # tiles, 3 per split.
+    assert oracle.split_ranges(1000, 1000, 64, 2, window=300) == [(640, 832), (832, 1000)]
+    # kv_len 450 of a 1000-key cache, W 300, 3 splits: first key 150 -> tile 2 (key 128); 2 tiles
+    # per split; the last split ends at the sequence.
+    assert oracle.split_ranges(450, 1000, 64, 3, window=300) == [(128, 256), (256, 384),
+                                                                 (384, 450)]
+    # A window longer than the sequence: the unwindowed ranges exactly.
+    assert oracle.split_ranges(100, 1000, 64, 2, window=5000) == [(0, 100), (100, 100)]
+    assert oracle.split_ranges(100, 1000, 64, 2, window=5000) == oracle.split_ranges(100, 1000,
+                                                                                     64, 2)
+    # One tile's worth of window ending on a tile boundary: a single tile, then one key more
+    # reaches into the next tile (span 2 tiles, one per split).
+    assert oracle.split_ranges(640, 640, 64, 1, window=64) == [(576, 640)]
+    assert oracle.split_ranges(641, 641, 64, 2, window=64) == [(576, 640), (640, 641)]
+    # A one-key window at the start of a tile; more splits than tiles leave empty splits.
+    assert oracle.split_ranges(129, 129, 64, 3, window=1) == [(128, 129), (129, 129), (129, 129)]
+    assert oracle.window_first_key(1000, 300) == 700
+    assert oracle.window_first_key(200, 300) == 0
+    assert oracle.window_first_key(200, 0) == 0
+
+
 def test_decode_units_and_splits_follow_closed_form():
     from flashattention_softmax_threshold_amd.inputs import decode_inputs
 
