@@ -45,8 +45,11 @@ EXPORTED = (
     "blasst_status_string", "blasst_resolve_lambda", "blasst_timestep_gate",
     "blasst_sparsity_curve", "blasst_fit_calibration",
     "blasst_prefill_tiles", "blasst_attn_prefill", "blasst_decode_plan",
-    "blasst_decode_workspace_size", "blasst_attn_decode",
+    "blasst_decode_workspace_size", "blasst_attn_decode", "blasst_attn_decode_noalloc",
 )
+
+# Bytes of the scratch array blasst_attn_decode_noalloc keeps per GPU (BLASST_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 
 class BlasstError(RuntimeError):
@@ -151,6 +154,8 @@ def load_library():
         lib.blasst_decode_workspace_size.restype = ctypes.c_size_t
         lib.blasst_attn_decode.argtypes = [ctypes.POINTER(_DecodeArgs), P, ctypes.c_size_t, P]
         lib.blasst_attn_decode.restype = ctypes.c_int
+        lib.blasst_attn_decode_noalloc.argtypes = [ctypes.POINTER(_DecodeArgs), P]
+        lib.blasst_attn_decode_noalloc.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -511,7 +516,7 @@ def blasst_attn_decode(q, k, v, *, kv_len=None, lam: float = 0.0, softmax_scale:
         shape = (B, Hkv, -(-(Hq // Hkv) // br), -(-L // bc))
         _check_out(tile_status, "tile_status", shape, torch.uint8, dev, contiguous=True)
         _check_out(tile_margin, "tile_margin", shape, torch.float32, dev, contiguous=True)
-    if workspace is not None:
+    if workspace is not None and workspace is not _NOALLOC:
         if workspace.device != dev:
             raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
         if not workspace.is_contiguous():
@@ -524,6 +529,10 @@ def blasst_attn_decode(q, k, v, *, kv_len=None, lam: float = 0.0, softmax_scale:
                      block_r=block_r, block_c=block_c, num_splits=num_splits,
                      block_table=block_table, max_kv_len=max_kv_len, window=window)
     lib = load_library()
+    if workspace is _NOALLOC:
+        _check(lib.blasst_attn_decode_noalloc(ctypes.byref(a), _stream_handle(stream)),
+               "blasst_attn_decode_noalloc")
+        return o
     need = int(lib.blasst_decode_workspace_size(ctypes.byref(a)))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -532,3 +541,22 @@ def blasst_attn_decode(q, k, v, *, kv_len=None, lam: float = 0.0, softmax_scale:
     _check(lib.blasst_attn_decode(ctypes.byref(a), ws_ptr, ws_bytes, _stream_handle(stream)),
            "blasst_attn_decode")
     return o
+
+
+_NOALLOC = object()
+
+
+def blasst_attn_decode_noalloc(q, k, v, *, o, kv_len=None, lam: float = 0.0,
+                               softmax_scale: float = 0.0, lse=None, counters=None,
+                               tile_status=None, tile_margin=None, block_r: int = 0,
+                               block_c: int = 0, num_splits: int = 0, block_table=None,
+                               max_kv_len=None, window: int = 0, stream=None):
+    """blasst_attn_decode with the split partials in the library's per-GPU scratch array: the
+    call allocates nothing (o must be given). Calls that overlap in time on one GPU race."""
+    if o is None:
+        raise ValueError("blasst_attn_decode_noalloc writes into a caller-provided o")
+    return blasst_attn_decode(q, k, v, kv_len=kv_len, lam=lam, softmax_scale=softmax_scale, o=o,
+                              lse=lse, counters=counters, tile_status=tile_status,
+                              tile_margin=tile_margin, block_r=block_r, block_c=block_c,
+                              num_splits=num_splits, workspace=_NOALLOC, block_table=block_table,
+                              max_kv_len=max_kv_len, window=window, stream=stream)

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libblasst.so")
-SOURCES = ["api.cpp", "prefill.hip", "prefill_mfma.hip", "decode.hip", "mla.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "prefill_mfma.hip", "decode.hip", "mla.hip", "noalloc.hip"]
 ARCH = os.environ.get("BLASST_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -323,8 +323,20 @@ size_t blasst_decode_workspace_size(const blasst_decode_args *a) {
   return ((o_bytes + 255) / 256) * 256 + ((l_bytes + 255) / 256) * 256;
 }
 
-blasst_status blasst_attn_decode(const blasst_decode_args *a, void *workspace,
-                                 size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace blasst {
+
+blasst_status decode_check(const blasst_decode_args *a) {
+  if (!a) return BLASST_ERR_INVALID_ARG;
+  if (!finite_nonneg(a->lambda)) return BLASST_ERR_INVALID_ARG;
+  if (!(a->softmax_scale >= 0.f) || !isfinite(a->softmax_scale)) return BLASST_ERR_INVALID_ARG;
+  int32_t br, bc, s;
+  return blasst_decode_plan(a, &br, &bc, &s);
+}
+
+blasst_status decode_with_workspace(const blasst_decode_args *a, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
   if (!a) return BLASST_ERR_INVALID_ARG;
   if (!finite_nonneg(a->lambda)) return BLASST_ERR_INVALID_ARG;
   if (!(a->softmax_scale >= 0.f) || !isfinite(a->softmax_scale)) return BLASST_ERR_INVALID_ARG;
@@ -395,4 +407,9 @@ blasst_status blasst_attn_decode(const blasst_decode_args *a, void *workspace,
   return err == hipSuccess ? BLASST_OK : BLASST_ERR_HIP;
 }
 
-}  // extern "C"
+}  // namespace blasst
+
+extern "C" blasst_status blasst_attn_decode(const blasst_decode_args *a, void *workspace,
+                                            size_t workspace_bytes, void *stream) {
+  return blasst::decode_with_workspace(a, workspace, workspace_bytes, stream);
+}

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "blasst.h"
+
 namespace blasst {
 
 // Key tile width of every kernel here (B_c).
@@ -73,4 +75,14 @@ hipError_t launch_decode_gqa(const DecodeParams &p, int head_dim, hipStream_t st
 hipError_t launch_decode_mla(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_split_combine(const DecodeParams &p, int head_dim_v, hipStream_t stream);
 
+}  // namespace blasst
+
+// Host path of a decode call, shared by blasst_attn_decode (caller's workspace) and
+// blasst_attn_decode_noalloc (the library's scratch array); defined in api.cpp.
+namespace blasst {
+// Argument and plan checks of a decode call (host only; no HIP call).
+blasst_status decode_check(const blasst_decode_args *a);
+// Checks, plans and launches a decode call with the given split workspace.
+blasst_status decode_with_workspace(const blasst_decode_args *a, void *workspace,
+                                    size_t workspace_bytes, void *stream);
 }  // namespace blasst

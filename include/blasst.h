@@ -261,6 +261,26 @@ size_t blasst_decode_workspace_size(const blasst_decode_args *args);
 blasst_status blasst_attn_decode(const blasst_decode_args *args, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Decode without any allocation, for callers that cannot call hipMalloc: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. The same call as
+ * blasst_attn_decode (same kernels, same results bit for bit), but the split partials live in a
+ * scratch array of BLASST_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; the caller passes inputs and outputs only.
+ *
+ *   - The stream must belong to the current HIP device (the scratch array used is that device's).
+ *     The first call on a device looks up the array's device address; no call allocates or
+ *     frees memory, and no call issues a memset or copy.
+ *   - A call whose blasst_decode_workspace_size exceeds BLASST_NOALLOC_SCRATCH_BYTES returns
+ *     BLASST_ERR_WORKSPACE before touching the device (ask for fewer splits, or use
+ *     blasst_attn_decode with a workspace). Other errors as for blasst_attn_decode.
+ *   - Every call on one GPU shares that GPU's array and leaves its partials there: calls that
+ *     overlap in time on one GPU (two streams, two host threads) race and give wrong results.
+ *     Calls ordered on one stream are safe.
+ * ------------------------------------------------------------------------------------------ */
+#define BLASST_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u) /* 128 MiB per GPU */
+blasst_status blasst_attn_decode_noalloc(const blasst_decode_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

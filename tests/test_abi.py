@@ -397,3 +397,28 @@ def test_decode_binding_checks_every_tensor_before_the_call():
     ]
     for exc, match, args, kw in bad:
         _expect(exc, match, F.blasst_attn_decode, *args, **kw)
+
+
+def test_noalloc_decode_refuses_partials_beyond_its_scratch_before_any_device_call():
+    """blasst_attn_decode_noalloc checks on the host that the split partials fit its scratch array
+    (BLASST_NOALLOC_SCRATCH_BYTES per GPU) and refuses a larger plan before touching the device."""
+    a = F._DecodeArgs()
+    a.dtype = F.BLASST_BF16
+    a.batch, a.heads_q, a.heads_kv, a.max_kv_len = 128, 128, 1, 65536
+    a.head_dim_qk, a.head_dim_v = 576, 512
+    a.q = a.o = 1 << 20
+    a.k = a.v = 1 << 21
+    a.q_stride[:] = [128 * 576, 576]
+    a.k_stride[:] = [65536 * 576, 576, 576]
+    a.v_stride[:] = [65536 * 576, 576, 576]
+    a.o_stride[:] = [128 * 512, 512]
+    a.num_splits = 8
+    lib = F.load_library()
+    assert lib.blasst_decode_workspace_size(ctypes.byref(a)) > F.NOALLOC_SCRATCH_BYTES
+    assert lib.blasst_attn_decode_noalloc(ctypes.byref(a), None) == F.BLASST_ERR_WORKSPACE
+    a.lam = float("nan")
+    assert lib.blasst_attn_decode_noalloc(ctypes.byref(a), None) == F.BLASST_ERR_INVALID_ARG
+    assert lib.blasst_attn_decode_noalloc(None, None) == F.BLASST_ERR_INVALID_ARG
+    text = open(os.path.join(ROOT, "include", "blasst.h")).read()
+    m = re.search(r"#define BLASST_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u\)", text)
+    assert m and int(m[1]) * int(m[2]) * int(m[3]) == F.NOALLOC_SCRATCH_BYTES
