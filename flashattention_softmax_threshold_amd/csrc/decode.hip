@@ -8,19 +8,21 @@
 //
 // Work unit (one workgroup, 4 waves): (split, KV head g, block of up to RB query heads that share
 // g, sequence b); the rows of a tile are those query heads. A "round" is 4 consecutive key tiles,
-// one per wave:
-//   1. each wave computes S^T = K Q^T for its tile with v_mfma_f32_16x16x32_bf16, the K fragments
-//      coming straight from HBM into registers (no LDS); then it requests the K tile of the next
-//      round, so K stays in flight while this round finishes;
+// one per wave. Every K and V tile goes from HBM straight into the wave's own LDS tiles
+// (global_load_lds_dwordx4), so no load is visible to the compiler and every wait is an explicit
+// count of the wave's copies in flight:
+//   1. each wave computes S^T = K Q^T for its tile with v_mfma_f32_16x16x32_bf16, K read from its
+//      LDS tile; then it requests the K tile of the next round into the same LDS tile;
 //   2. tile row maxima meet in LDS; every wave forms the same running (prefix) maxima over the 4
 //      tiles in key order, the same per-tile votes and the round maximum M;
-//   3. a wave whose tile is kept requests its V tile only now, straight from HBM into its own LDS
-//      tile (global_load_lds_dwordx4); skipped tiles load no V at all. It forms P = exp2(S - M)
-//      in bf16 from its score registers, which are already the B operand layout of
-//      v_mfma_f32_16x16x32_bf16, and accumulates O^T += V^T P^T on the matrix cores, V^T read
-//      from the LDS tile with ds_read_b64_tr_b16 (16 MFMAs per tile at d = 128 for any number of
-//      rows; the same product on the vector ALUs would take rows x d x 64 multiply-adds);
+//   3. the wave accumulates O^T += V^T P^T for its kept tile of the PREVIOUS round (V^T read from
+//      its LDS V tile with ds_read_b64_tr_b16, P kept in registers in the B operand layout of the
+//      16x16x32 MFMA); O and l move to M; if this round's tile is kept it forms P = exp2(S - M)
+//      in bf16 and only now requests its V tile. Skipped tiles load no V at all.
 //   4. at the end the 4 waves' partial O and l are summed through LDS.
+// A kept tile's V is thus consumed one round after it is requested, behind the next round's
+// scores and vote, instead of being waited for in the round that asked for it; the terms enter O
+// in the same order as when each round consumed its own V (bit-identical results).
 // Using the round maximum M for P (instead of re-scaling tile by tile) is the same online
 // softmax in exact arithmetic; the skip decisions use each tile's own prefix maximum.
 #include "internal.h"
@@ -41,26 +43,33 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Waits until at most N of this wave's vector memory loads are outstanding (s_waitcnt with
+// vmcnt = N; the export and LDS counters are left at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Two workgroups per CU (at most 256 registers per wave; about 200 are used at d = 128 for any
-// number of rows, since O lives in 16x16 MFMA accumulators): twice the K and V loads in flight,
-// which the skip case (V requested only after the vote) and the paged cache (page-number reads)
-// need.
+// LDS holds a K and a V tile per wave: 128 KiB per workgroup at d = 128 (one workgroup per CU,
+// each wave with up to 32 KiB of copies in flight), 64 KiB at d = 64 (two per CU).
 template <int D, int RB, bool PAGED>
-__global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void decode_gqa_kernel(DecodeParams p) {
   constexpr int STEPS = D / 32;  // k-steps of one 16x16x32 MFMA chain
   constexpr int CPR = D / 8;     // 16-byte chunks per key row
   constexpr int ROWB = 2 * D;    // bytes of a key row
-  constexpr int RPL = 1024 / ROWB;            // V rows one wave-wide 16-byte copy fills
-  constexpr int VLD = kBlockC / RPL;          // V copies per wave per tile
+  constexpr int RPL = 1024 / ROWB;            // key rows one wave-wide 16-byte copy fills
+  constexpr int NLD = kBlockC / RPL;          // copies per wave per K or V tile
   constexpr int RPB = 256 / ROWB;             // key rows per 256 bytes of LDS banks
-  // Each wave's V tile (64 keys x D, bf16) in LDS, 16-byte chunks XOR-swizzled by the row; the
-  // same memory holds the waves' partial O for the final sum.
+  // Each wave's K and V tiles (64 keys x D, bf16) in LDS, 16-byte chunks XOR-swizzled by the
+  // row; the V tiles' memory holds the waves' partial O for the final sum.
+  __shared__ __attribute__((aligned(1024))) char sK[4][kBlockC * ROWB];
   __shared__ __attribute__((aligned(1024))) char sV[4][kBlockC * ROWB];
   static_assert(sizeof(float) * 4 * RB * D <= sizeof(sV), "partial O must fit in the V tiles");
   float(*sO)[RB][D] = reinterpret_cast<float(*)[RB][D]>(&sV[0][0]);
@@ -70,6 +79,9 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
   // Chunk c of key row r sits at chunk c ^ vswz(r): 8 consecutive rows reading the same
   // 32-byte column window (a transposing read) cover all 64 banks.
   auto vswz = [&](int r) { return 2 * ((r / RPB) % (CPR / 2)); };
+  // K: chunk c of row r at c ^ (r % CPR): the 16 rows of one score k-step read 16 distinct
+  // 16-byte bank slots.
+  auto kswz = [&](int r) { return r & (CPR - 1); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,10 +112,10 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
       (const __bf16 *)p.k + (PAGED ? 0 : b * p.k_sb) + g * p.k_sh;
   const __bf16 *__restrict__ Vg =
       (const __bf16 *)p.v + (PAGED ? 0 : b * p.v_sb) + g * p.v_sh;
-  // Paged: each lane holds the page of key `lane` of a tile, loaded one round before the tile is
-  // read (loads complete in issue order, so a table read issued just before the K or V loads
-  // would make them wait for every load in flight); a row's page comes from the lane that holds
-  // it with one cross-lane read.
+  // Paged: each lane holds the page of key `lane` of a tile, read at the top of the round before
+  // the tile's copies are issued (the compiler waits for that read, and with it for every copy
+  // issued before it, before the page is first used); a row's page comes from the lane that
+  // holds it with one cross-lane read.
   const int32_t *__restrict__ bt = PAGED ? p.block_table + (int64_t)b * p.pages_per_seq : nullptr;
   const int pmask = (1 << p.page_shift) - 1;
   auto page_of_lane_key = [&](int tile) -> int {  // page of key tile * 64 + lane (clamped)
@@ -136,18 +148,30 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
       qf[s] = ok ? *(const bf16x8_t *)(qrow + 32 * s + 8 * kgrp) : (bf16x8_t)(__bf16)0.f;
   }
 
-  bf16x8_t kreg[4 * STEPS];
-  auto load_k = [&](int t, int pages) {
+  // K and V copies, straight from HBM into this wave's LDS tiles (global_load_lds_dwordx4): lane L
+  // of copy kk fills row kk * RPL + L / CPR at physical chunk L % CPR with logical chunk
+  // (L % CPR) ^ swizzle(row); keys past the sequence copy its last row (their scores are masked
+  // and their P is 0).
+  const uint32_t sk_base = lds_addr(&sK[wv][0]);
+  const uint32_t sv_base = lds_addr(&sV[wv][0]);
+  auto copy_tile = [&](const __bf16 *base, int64_t sb, int64_t ss, int t, int pages,
+                       uint32_t lds, bool is_v) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = t * kBlockC + 16 * kb + n;
-      const int64_t off = row_off(key, pages, p.k_sb, p.k_ss);
-#pragma unroll
-      for (int s = 0; s < STEPS; ++s)
-        kreg[kb * STEPS + s] = key < seq_len
-                                   ? *(const bf16x8_t *)(Kg + off + 32 * s + 8 * kgrp)
-                                   : (bf16x8_t)(__bf16)0.f;
+    for (int kk = 0; kk < NLD; ++kk) {
+      const int r = kk * RPL + lane / CPR;
+      const int key = min(t * kBlockC + r, seq_len - 1);
+      const int64_t off = row_off(key, pages, sb, ss);
+      const int sw = is_v ? vswz(r) : kswz(r);
+      lds_dma16(base + off + 8 * ((lane % CPR) ^ sw), lds + kk * 1024);
     }
+  };
+  auto load_k = [&](int t, int pages) { copy_tile(Kg, p.k_sb, p.k_ss, t, pages, sk_base, false); };
+  auto load_v = [&](int t, int pages) { copy_tile(Vg, p.v_sb, p.v_ss, t, pages, sv_base, true); };
+  // K operand of S^T = K Q^T (16 keys x 32 head dims per MFMA): lane (n, kgrp) reads key
+  // 16 kb + n, logical chunk 4 s + kgrp.
+  auto rdk = [&](int kb, int s) {
+    const int r = 16 * kb + n;
+    return *(const bf16x8_t *)(&sK[wv][r * ROWB + 16 * ((4 * s + kgrp) ^ kswz(r))]);
   };
 
   // O^T = V^T P^T on the matrix cores: oacc[db] holds head dims 16 db + 4 kgrp .. + 3 of query
@@ -155,48 +179,66 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
   f32x4_t oacc[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) oacc[db] = (f32x4_t)0.f;
-  // V copy of load kk: lane L fills row kk * RPL + L / CPR at physical chunk L % CPR with logical
-  // chunk (L % CPR) ^ vswz(row); keys past the sequence copy its last row (their P is 0).
-  const uint32_t sv_base = lds_addr(&sV[wv][0]);
-  auto load_v = [&](int t, int pages) {
-#pragma unroll
-    for (int kk = 0; kk < VLD; ++kk) {
-      const int r = kk * RPL + lane / CPR;
-      const int key = min(t * kBlockC + r, seq_len - 1);
-      const int64_t off = row_off(key, pages, p.v_sb, p.v_ss);
-      lds_dma16(Vg + off + 8 * ((lane % CPR) ^ vswz(r)), sv_base + kk * 1024);
-    }
-  };
   // Transposing V reads: for k-step ks (keys 32 ks ..) and column block db, source lane L points at
   // key 32 ks + 4 (L / 16) + (L % 16) / 4 (+ 16 for the second read), head dims
   // 16 db + 4 (L % 4) .. + 3; lane L then receives head dim 16 db + L % 16 at the keys
   // 32 ks + 4 (L / 16) + 0..3 (and + 16), the key order of the P fragments.
   const int tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2);
   const int tr_cb = lane & 3;
+  bf16x8_t pb[2];  // P of this wave's last kept tile: B operands of its two 32-key k-steps
+  auto pv = [&]() {
+    const char *vt = &sV[wv][0];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const int r0 = 32 * ks + tr_row, r1 = r0 + 16;
+        const int c = 2 * db + (tr_cb >> 1);
+        const char *p0 = vt + r0 * ROWB + 16 * (c ^ vswz(r0)) + 8 * (tr_cb & 1);
+        const char *p1 = vt + r1 * ROWB + 16 * (c ^ vswz(r1)) + 8 * (tr_cb & 1);
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
+        const bf16x8_t va =
+            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ks], oacc[db], 0, 0, 0);
+      }
+    }
+  };
   float l_part = 0.f;
   float m_run = -INFINITY;
   unsigned visited = 0, skipped = 0;
   const int n_rounds = t_end > t_begin ? (t_end - t_begin + 3) / 4 : 0;
 
+  // Copy order of a wave: K of round 0; then per round r, K of round r + 1 (after the scores of
+  // round r) and V of round r (after the vote, kept tiles only). So at the top of round r the
+  // wave's outstanding copies are K_r and then (if its tile of round r - 1 was kept) V_{r-1}, and
+  // at the P.V of round r - 1 they are V_{r-1} and then K_{r+1} (if any): the waits below count
+  // copies accordingly (vmcnt counts this wave's loads, which complete in issue order).
   if (n_rounds > 0 && t_begin + wv < t_end) {
     pages_cur = page_of_lane_key(t_begin + wv);
     load_k(t_begin + wv, pages_cur);
   }
+  bool pv_pending = false;  // the wave's tile of the previous round was kept: V in sV, P in pb
 
   for (int r = 0; r < n_rounds; ++r) {
     const int t = t_begin + 4 * r + wv;
     const bool have = t < t_end;
-    if (PAGED && t + 4 < t_end) pages_next = page_of_lane_key(t + 4);  // first load of the round
+    if (pv_pending)
+      wait_vmcnt<NLD>();  // K_r has landed; V_{r-1} may still be in flight
+    else
+      wait_vmcnt<0>();
+    wave_lds_sync();
+    if (PAGED && t + 4 < t_end) pages_next = page_of_lane_key(t + 4);
     f32x4_t sacc[4];
     float mt = -INFINITY;
+    const bool next_k = have && t + 4 < t_end;
     if (have) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         sacc[kb] = (f32x4_t)0.f;
 #pragma unroll
         for (int s = 0; s < STEPS; ++s)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[kb * STEPS + s], qf[s], sacc[kb],
-                                                              0, 0, 0);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdk(kb, s), qf[s], sacc[kb], 0, 0, 0);
       }
       if ((t + 1) * kBlockC > seq_len || t * kBlockC < first_key) {
 #pragma unroll
@@ -211,7 +253,9 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sacc[kb][i]);
-      if (t + 4 < t_end) load_k(t + 4, pages_next);  // next round's K, in flight meanwhile
+      // The next round's K goes into the same LDS tile: every read of this one has been
+      // consumed by the MFMAs above.
+      if (next_k) load_k(t + 4, pages_next);
     } else {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) sacc[kb] = (f32x4_t)0.f;
@@ -239,20 +283,26 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
     const float M = mp;
     const bool my_keep = have && keep_w[wv];
 
-    // V tile only for a kept tile, straight into this wave's LDS tile.
-    if (my_keep) load_v(t, pages_cur);
+    // P.V of the wave's kept tile of the previous round, into O still scaled to that round's max.
+    if (pv_pending) {
+      if (next_k)
+        wait_vmcnt<NLD>();  // V_{r-1} has landed; K_{r+1} may still be in flight
+      else
+        wait_vmcnt<0>();
+      wave_lds_sync();
+      pv();
+    }
+    // Move O and l to this round's max; a kept tile's P = exp2(S - M) in bf16 as the B operands
+    // of its two 32-key k-steps (elements 0..3 are the keys of block 2 ks, 4..7 those of block
+    // 2 ks + 1, this lane's 4 keys of each); its V is requested now and used next round.
     const float M_use = (M == -INFINITY) ? 0.f : M;
     const float alpha = exp2_fast(m_run - M_use);  // for this lane's row n
     l_part *= alpha;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
-
     if (my_keep) {
-      // P = exp2(S - M) in bf16 as the B operands of the two 32-key k-steps: elements 0..3 are
-      // the keys of block 2 ks, 4..7 those of block 2 ks + 1 (this lane's 4 keys of each).
       const bool row_live = n < nrows;
       const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
-      bf16x8_t pb[2];
       float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -269,25 +319,9 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
         ps1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, ps1, false);
       }
       l_part += ps0 + ps1;
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's V copies have landed in its LDS tile
-      wave_lds_sync();
-      const char *vt = &sV[wv][0];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          const int r0 = 32 * ks + tr_row, r1 = r0 + 16;
-          const int c = 2 * db + (tr_cb >> 1);
-          const char *p0 = vt + r0 * ROWB + 16 * (c ^ vswz(r0)) + 8 * (tr_cb & 1);
-          const char *p1 = vt + r1 * ROWB + 16 * (c ^ vswz(r1)) + 8 * (tr_cb & 1);
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
-          const bf16x8_t va =
-              __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ks], oacc[db], 0, 0, 0);
-        }
-      }
+      load_v(t, pages_cur);  // the previous V tile's reads were consumed by pv() above
     }
+    pv_pending = my_keep;
     m_run = M;
     if constexpr (PAGED) pages_cur = pages_next;
 
@@ -304,6 +338,12 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeParams p) {
       }
     }
   }
+  if (pv_pending) {  // the last kept tile's P.V
+    wait_vmcnt<0>();
+    wave_lds_sync();
+    pv();
+  }
+  wait_vmcnt<0>();
 
   // ---- Sum the waves' partials; write O (unsplit) or the split's partial.
   __syncthreads();  // every wave's last V reads are done: the V tiles become sO
