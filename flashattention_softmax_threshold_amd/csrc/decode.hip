@@ -112,10 +112,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void decode_gqa_kernel(Decode
       (const __bf16 *)p.k + (PAGED ? 0 : b * p.k_sb) + g * p.k_sh;
   const __bf16 *__restrict__ Vg =
       (const __bf16 *)p.v + (PAGED ? 0 : b * p.v_sb) + g * p.v_sh;
-  // Paged: each lane holds the page of key `lane` of a tile, read at the top of the round before
-  // the tile's copies are issued (the compiler waits for that read, and with it for every copy
-  // issued before it, before the page is first used); a row's page comes from the lane that
-  // holds it with one cross-lane read.
+  // Paged: each lane holds the page of key `lane` of a tile, read two rounds before the tile's
+  // copies are issued (the compiler waits for such a read, and with it for every copy issued
+  // before it, before the page is first used); a row's page comes from the lane that holds it
+  // with one cross-lane read.
   const int32_t *__restrict__ bt = PAGED ? p.block_table + (int64_t)b * p.pages_per_seq : nullptr;
   const int pmask = (1 << p.page_shift) - 1;
   auto page_of_lane_key = [&](int tile) -> int {  // page of key tile * 64 + lane (clamped)
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void decode_gqa_kernel(Decode
       return (int64_t)key * ss;
     }
   };
-  int pages_cur = 0, pages_next = 0;  // paged: this round's tile, the next round's tile
+  int pages_cur = 0, pages_next = 0, pages_nn = 0;  // paged: the tiles of rounds r, r + 1, r + 2
   const int64_t unit_tiles =
       (((int64_t)b * p.Hkv + g) * p.n_rblocks + rb) * (int64_t)p.n_tiles;
 
@@ -216,6 +216,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void decode_gqa_kernel(Decode
   // copies accordingly (vmcnt counts this wave's loads, which complete in issue order).
   if (n_rounds > 0 && t_begin + wv < t_end) {
     pages_cur = page_of_lane_key(t_begin + wv);
+    if (PAGED && t_begin + wv + 4 < t_end) pages_next = page_of_lane_key(t_begin + wv + 4);
     load_k(t_begin + wv, pages_cur);
   }
   bool pv_pending = false;  // the wave's tile of the previous round was kept: V in sV, P in pb
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void decode_gqa_kernel(Decode
     else
       wait_vmcnt<0>();
     wave_lds_sync();
-    if (PAGED && t + 4 < t_end) pages_next = page_of_lane_key(t + 4);
+    if (PAGED && t + 8 < t_end) pages_nn = page_of_lane_key(t + 8);  // used two rounds on
     f32x4_t sacc[4];
     float mt = -INFINITY;
     const bool next_k = have && t + 4 < t_end;
@@ -292,9 +293,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void decode_gqa_kernel(Decode
       wave_lds_sync();
       pv();
     }
+    // A kept tile's V is requested now (the previous V tile's reads were consumed by pv() above)
+    // and used next round.
+    if (my_keep) load_v(t, pages_cur);
     // Move O and l to this round's max; a kept tile's P = exp2(S - M) in bf16 as the B operands
     // of its two 32-key k-steps (elements 0..3 are the keys of block 2 ks, 4..7 those of block
-    // 2 ks + 1, this lane's 4 keys of each); its V is requested now and used next round.
+    // 2 ks + 1, this lane's 4 keys of each).
     const float M_use = (M == -INFINITY) ? 0.f : M;
     const float alpha = exp2_fast(m_run - M_use);  // for this lane's row n
     l_part *= alpha;
@@ -319,11 +323,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void decode_gqa_kernel(Decode
         ps1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, ps1, false);
       }
       l_part += ps0 + ps1;
-      load_v(t, pages_cur);  // the previous V tile's reads were consumed by pv() above
     }
     pv_pending = my_keep;
     m_run = M;
-    if constexpr (PAGED) pages_cur = pages_next;
+    if constexpr (PAGED) {
+      pages_cur = pages_next;
+      pages_next = pages_nn;
+    }
 
     if (have) {
       ++visited;
