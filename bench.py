@@ -72,7 +72,8 @@ def _parse():
                     help="headline: the Video-DiT call only; prefill / decode / mla / tiny: that "
                          "workload only (profiling runs isolate one kernel this way)")
     ap.add_argument("--a", type=float, default=None,
-                    help="decode parts: time only lambda = a / L instead of the sweep")
+                    help="prefill / decode / mla parts: time only lambda = a / L instead of the "
+                         "sweep")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes three times "
                          "(the reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -345,11 +346,14 @@ def _prefill_part(F, torch, args, dev, stream, out):
                 "dense_tflops": dense_flops / (ms * 1e-3) / 1e12, "executed_tflops": ex,
                 "mfma_frac": ex / BF16_PEAK_TFLOPS, "ceiling_2/(2-f)": 2.0 / (2.0 - sa / va)}
 
-    pts = [point(0.0, "0")]
-    for a in (4.0, 16.0, 64.0):
-        pts.append(point(a / L, f"{int(a)}/L"))
-    for pt in pts:
-        pt["speedup_vs_lambda0"] = pts[0]["ms"] / pt["ms"]
+    if args.a is not None:  # one threshold only (counter passes)
+        pts = [point(args.a / L, f"{args.a:g}/L")]
+    else:
+        pts = [point(0.0, "0")]
+        for a in (4.0, 16.0, 64.0):
+            pts.append(point(a / L, f"{int(a)}/L"))
+        for pt in pts:
+            pt["speedup_vs_lambda0"] = pts[0]["ms"] / pt["ms"]
     _progress("prefill causal GQA: " + ", ".join(f"{p_['lambda']} {p_['ms']:.4f} ms"
                                                  for p_ in pts))
     res = {"workload": "causal GQA prefill B1 Hq32/Hkv8 L8192 d128 bf16, tile 128x64, "
@@ -357,7 +361,7 @@ def _prefill_part(F, torch, args, dev, stream, out):
            "points": pts,
            "traffic_lambda_16/L": _traffic_from_profile(
                "prefill_mfma.hip", "prefill_mfma_causal_L8192_hbm_counters.json")}
-    if args.part in ("all", "prefill"):
+    if args.part in ("all", "prefill") and args.a is None:
         # Speedup against skip fraction: thresholds at quantiles of the tile margins of one
         # lambda = 0 call (a tile is skipped exactly when its margin is below ln lambda).
         from flashattention_softmax_threshold_amd import calibration as C
