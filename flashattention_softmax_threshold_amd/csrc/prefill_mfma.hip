@@ -32,6 +32,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace blasst {
 namespace {
 
@@ -199,6 +201,20 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
   };
   auto issue_k = [&](int j, int st) { issue(j, st, 0); };
   auto issue_v = [&](int j, int st) { issue(j, st, 1); };
+  // Steps whose copies are all full tiles take them from running tile pointers (one 64-bit
+  // scalar add per tile instead of a multiply and a bounds test per copy).
+  const int n_full = p.Lkv / kBlockC;  // tiles with no row past the end
+  const char *kt_run = (const char *)(Kg + (int64_t)(j0 + 2) * kBlockC * p.k_ss);
+  const char *vt_run = (const char *)(Vg + (int64_t)(j0 + 1) * kBlockC * p.v_ss);
+  const int64_t k_tile_bytes = (int64_t)kBlockC * p.k_ss * 2;
+  const int64_t v_tile_bytes = (int64_t)kBlockC * p.v_ss * 2;
+  auto issue_full = [&](const char *tb, int st, int op) {
+#pragma unroll
+    for (int t2 = 0; t2 < G::LOADS_PER_WAVE; ++t2) {
+      const int ii = wv * G::LOADS_PER_WAVE + t2;
+      lds_dma16_s(tb, op ? v_off[t2] : k_off[t2], lds_addr(&smem[st][op][ii * 1024]));
+    }
+  };
 
   // Per-lane LDS offsets of the MFMA operands.
   // K (A operand of S^T): row 32 kb + n, logical chunk 2 s + hh.
@@ -228,7 +244,8 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
   // hides behind matrix work; the scheduling hints keep that order. With vj >= 0 the copies of
   // V_vj and K_{vj+1} are issued between the MFMAs (after the second and the fourth k-step): a
   // wave held up issuing them still has MFMAs in flight.
-  auto compute_s = [&](int st, f32x16_t *sacc, int vj = -1) {
+  auto compute_s = [&](auto full_c, int st, f32x16_t *sacc, int vj = -1) {
+    constexpr bool FULL = decltype(full_c)::value;
     constexpr int NS = D / 16;  // k-steps
     // The V copy goes out after k-step 1 and the K copy after k-step 3: both need four k-steps.
     static_assert(NS >= 4, "the in-loop copies need at least four k-steps (D >= 64)");
@@ -250,8 +267,13 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s][kb], qf[s], sacc[kb], 0, 0, 0);
-      if (s == 1 && vj >= 0) issue_v(vj, vj & 1);
-      if (s == 3 && vj >= 0 && vj + 1 < n_tiles) issue_k(vj + 1, (vj + 1) & 1);
+      if constexpr (FULL) {
+        if (s == 1) issue_full(vt_run, vj & 1, 1);
+        if (s == 3) issue_full(kt_run, (vj + 1) & 1, 0);
+      } else {
+        if (s == 1 && vj >= 0) issue_v(vj, vj & 1);
+        if (s == 3 && vj >= 0 && vj + 1 < n_tiles) issue_k(vj + 1, (vj + 1) & 1);
+      }
     }
     // Scheduling: KPF steps of reads first, then (2 MFMAs, 2 reads) pairs, then the tail MFMAs.
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * KPF, 0);
@@ -403,7 +425,8 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
   // kept) it exponentiates tile j-1 and accumulates P_{j-1} V_{j-1}; finally it votes on tile j.
   // K_{j+1} and V_j are loaded meanwhile (two LDS stages each). The scores alternate between two
   // register sets, so no step copies them.
-  auto step = [&](int j, f32x16_t *cur, const f32x16_t *prev) {
+  auto step = [&](auto full_c, int j, f32x16_t *cur, const f32x16_t *prev) {
+    constexpr bool FULL = decltype(full_c)::value;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's K_j and V_{j-1} have landed
     __syncthreads();                // ... and every wave's; votes for tile j-1 are visible
     const int4 vt = read_votes(j - 1);
@@ -416,7 +439,11 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
     }
     const int keep_prev = decision(j - 1, vt);
     const float m_prev = m_run;
-    compute_s(j & 1, cur, NH == 2 ? j : -1);
+    compute_s(full_c, j & 1, cur, NH == 2 ? j : -1);
+    if constexpr (FULL) {
+      kt_run += k_tile_bytes;
+      vt_run += v_tile_bytes;
+    }
     mask_tile(j, cur);
     if (keep_prev) {
       rescale_to(m_prev);
@@ -444,16 +471,25 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
   __syncthreads();
   if (n_tiles > j0 + 1) issue_k(j0 + 1, (j0 + 1) & 1);
   issue_v(j0, j0 & 1);
-  compute_s(j0 & 1, sa);
+  compute_s(std::false_type{}, j0 & 1, sa);
   mask_tile(j0, sa);
   publish_margin(j0, vote_tile(j0, sa));
   int j = j0 + 1;
+  // Two units per workgroup: pairs of steps whose copies (V_j, K_{j+1}, V_{j+1}, K_{j+2}) are
+  // all full tiles first, then the rest. (The one-unit kernel keeps the general copies: the
+  // extra loop copy there adds 4 bytes of spill.)
+  if constexpr (NH == 2) {
+    for (; j + 2 < n_tiles && j + 3 <= n_full; j += 2) {
+      step(std::true_type{}, j, sb, sa);
+      step(std::true_type{}, j + 1, sa, sb);
+    }
+  }
   for (; j + 1 < n_tiles; j += 2) {
-    step(j, sb, sa);
-    step(j + 1, sa, sb);
+    step(std::false_type{}, j, sb, sa);
+    step(std::false_type{}, j + 1, sa, sb);
   }
   if (j < n_tiles) {
-    step(j, sb, sa);
+    step(std::false_type{}, j, sb, sa);
     finish(sb);
   } else {
     finish(sa);
