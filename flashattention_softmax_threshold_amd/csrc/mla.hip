@@ -34,6 +34,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace blasst {
 namespace {
 
@@ -147,6 +149,11 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
       qf[s] = row_ok ? *(const bf16x8_t *)(qrow + 16 * s + 8 * hh) : (bf16x8_t)(__bf16)0.f;
+    // The first 24 k-steps' fragments live in the accumulation registers (an MFMA takes its B
+    // operand from either register file), which leaves VGPRs for K fragments read 6 k-steps
+    // ahead.
+#pragma unroll
+    for (int s = 0; s < 24; ++s) asm volatile("" : "+a"(qf[s]));
   }
 
   // Tile loads: wave load nn < 16 copies latent row i = wv + 4 nn (chunk L ^ lat_swz(i) of the
@@ -185,6 +192,39 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     }
   };
 
+  // Full tiles of a contiguous cache (no row past the sequence): latent row i of the tile sits
+  // at a wave-uniform address (tile base + i rows), so a copy costs a 64-bit scalar add and the
+  // lane's chunk offset, one of four per wave: i = wv + 4 nn has lat_swz(i) = 4 wv + nn % 4. The
+  // rotary parts take a per-lane 32-bit offset from the tile base when 64 rows fit in 32 bits.
+  const int64_t row_bytes = p.k_ss * 2;
+  const bool off32 = !PAGED && row_bytes * kBlockC <= 0x7fffffffll;
+  uint32_t lat_off[4], rope_voff[2];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) lat_off[q4] = (uint32_t)((lane ^ (4 * wv + q4)) << 4);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int jr = wv + NW * h2;
+    rope_voff[h2] = (uint32_t)((8 * jr + (lane >> 3)) * row_bytes) + (uint32_t)kLatBytes +
+                    (uint32_t)(16 * ((lane & 7) ^ (lane >> 3)));
+  }
+  // cur: this wave's next latent row (advanced by 4 rows per copy); tb: the tile's first row.
+  auto issue_full = [&](const char *&cur, const char *tb, int st, int nn) {
+    const uint32_t lds_st = lds_addr(&smem[st][0]);
+    if (nn < kRowLoads / NW) {
+      const int i = wv + NW * nn;
+      lds_dma16_s(cur, lat_off[nn & 3], lds_st + i * kLatBytes);
+      cur += NW * row_bytes;
+    } else {
+      const int h2 = nn - kRowLoads / NW;
+      lds_dma16_s(tb, rope_voff[h2], lds_st + kRopeOff + (wv + NW * h2) * 1024);
+    }
+  };
+  // Copy mode of the next tile: 0 none, 1 full contiguous tile, 2 any other.
+  auto copy_mode = [&](int tile) -> int {
+    if (tile < 0) return 0;
+    return (off32 && (tile + 1) * kBlockC <= seq_len) ? 1 : 2;
+  };
+
   // O^T of this wave's 128 columns for both row groups of the unit: oacc[r][db] holds columns
   // 128 wv + 32 db .. + 31 of heads 32 r .. + 31.
   f32x16_t oacc[2][kDvBlocks];
@@ -216,8 +256,11 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     for (int b8 = 0; b8 < 8; ++b8) s_off[b8] = (uint32_t)(r * kLatBytes) + ((32u * b8) ^ g16);
     rope_off = (uint32_t)(kRopeOff + r * kRopeBytes) | (uint32_t)((hb ^ (r & 7)) << 4);
   }
-  auto compute_s = [&](int st, int next_tile, int next_pages) {
-    constexpr int KPF = 2;
+  auto compute_s = [&](auto mode_c, int st, int next_tile, int next_pages) {
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr int KPF = 6;
+    const char *tb = (const char *)(Kg + (int64_t)next_tile * kBlockC * p.k_ss);
+    const char *cur = tb + (int64_t)wv * row_bytes;
     f32x16_t sacc = (f32x16_t)0.f;
     const char *sm = smem[st];
     const char *lat[8];
@@ -234,7 +277,11 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     for (int s2 = 0; s2 < kSteps; ++s2) {
       if (s2 + KPF < kSteps) fr[s2 + KPF] = rdk(s2 + KPF);
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s2], qf[s2], sacc, 0, 0, 0);
-      if ((s2 & 1) && next_tile >= 0) issue_one(next_tile, st ^ 1, s2 >> 1, next_pages);
+      if constexpr (MODE == 1) {
+        if (s2 & 1) issue_full(cur, tb, st ^ 1, s2 >> 1);
+      } else if constexpr (MODE == 2) {
+        if (s2 & 1) issue_one(next_tile, st ^ 1, s2 >> 1, next_pages);
+      }
     }
     return sacc;
   };
@@ -357,7 +404,15 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     __syncthreads();
     const int pages_next = ahead;  // landed: the wait above drained every load
     if (PAGED && j + 2 < n_tiles) ahead = page_of_lane_key(t_begin + j + 2);
-    f32x16_t sacc = compute_s(j & 1, j + 1 < n_tiles ? t_begin + j + 1 : -1, pages_next);
+    const int nt = j + 1 < n_tiles ? t_begin + j + 1 : -1;
+    const int cm = copy_mode(nt);
+    f32x16_t sacc;
+    if (cm == 1)
+      sacc = compute_s(std::integral_constant<int, 1>{}, j & 1, nt, pages_next);
+    else if (cm == 2)
+      sacc = compute_s(std::integral_constant<int, 2>{}, j & 1, nt, pages_next);
+    else
+      sacc = compute_s(std::integral_constant<int, 0>{}, j & 1, nt, pages_next);
     mask_tile(t_begin + j, sacc);
     {
       float m[6];
@@ -401,8 +456,12 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
         const float a0 = rg == 0 ? alpha : alpha_o, a1 = rg == 0 ? alpha_o : alpha;
 #pragma unroll
         for (int db = 0; db < kDvBlocks; ++db) {
+          // O^T stays in the accumulation registers outside this branch; unpinned, the compiler
+          // copied all 128 of its registers to VGPRs at the top of every tile for it.
+          asm volatile("" : "+a"(oacc[0][db]), "+a"(oacc[1][db]));
           oacc[0][db] *= a0;
           oacc[1][db] *= a1;
+          asm volatile("" : "+a"(oacc[0][db]), "+a"(oacc[1][db]));
         }
         m_ref = m_run;
         m_ref_o = m_run_o;
