@@ -149,11 +149,6 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
       qf[s] = row_ok ? *(const bf16x8_t *)(qrow + 16 * s + 8 * hh) : (bf16x8_t)(__bf16)0.f;
-    // The first 24 k-steps' fragments live in the accumulation registers (an MFMA takes its B
-    // operand from either register file), which leaves VGPRs for K fragments read 6 k-steps
-    // ahead.
-#pragma unroll
-    for (int s = 0; s < 24; ++s) asm volatile("" : "+a"(qf[s]));
   }
 
   // Tile loads: wave load nn < 16 copies latent row i = wv + 4 nn (chunk L ^ lat_swz(i) of the
@@ -240,9 +235,9 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 
   // S^T for this wave's 32 heads and its 32 keys (key half kh): A = K rows 32 kh + n of stage st,
   // B = the wave's query fragments; 36 k-steps, K fragments read KPF steps ahead. The next tile's
-  // copies: a full contiguous tile's go out after the last K read, while the final MFMAs run, so
-  // their LDS writes do not compete with the K reads (about 4 % faster than one copy per two
-  // k-steps); the other copies go out one per two k-steps between the MFMAs.
+  // loads (next_tile >= 0) go out one per two k-steps between the MFMAs: each inline-asm load is
+  // a scheduling boundary, so the reads and MFMAs between two loads stay in source order, and a
+  // wave (alone on its SIMD) never stalls on a full load queue with its matrix core idle.
   // K reads of S: k-step s of this lane (row r = 32 kh + lane % 32, hb = lane / 32) reads
   // logical chunk 2 s + hb; for s < 32 that is physical chunk (2 s) ^ g, g = hb ^ lat_swz(r),
   // i.e. byte 256 (s / 8) + (32 (s % 8) ^ 16 g) of the row: eight per-lane offsets, computed
@@ -277,13 +272,11 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
     for (int s2 = 0; s2 < kSteps; ++s2) {
       if (s2 + KPF < kSteps) fr[s2 + KPF] = rdk(s2 + KPF);
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s2], qf[s2], sacc, 0, 0, 0);
-      if constexpr (MODE == 2) {
+      if constexpr (MODE == 1) {
+        if (s2 & 1) issue_full(cur, tb, st ^ 1, s2 >> 1);
+      } else if constexpr (MODE == 2) {
         if (s2 & 1) issue_one(next_tile, st ^ 1, s2 >> 1, next_pages);
       }
-    }
-    if constexpr (MODE == 1) {
-#pragma unroll
-      for (int nn = 0; nn < kLoadsPerTile / NW; ++nn) issue_full(cur, tb, st ^ 1, nn);
     }
     return sacc;
   };
@@ -458,12 +451,8 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
         const float a0 = rg == 0 ? alpha : alpha_o, a1 = rg == 0 ? alpha_o : alpha;
 #pragma unroll
         for (int db = 0; db < kDvBlocks; ++db) {
-          // O^T stays in the accumulation registers outside this branch; unpinned, the compiler
-          // copied all 128 of its registers to VGPRs at the top of every tile for it.
-          asm volatile("" : "+a"(oacc[0][db]), "+a"(oacc[1][db]));
           oacc[0][db] *= a0;
           oacc[1][db] *= a1;
-          asm volatile("" : "+a"(oacc[0][db]), "+a"(oacc[1][db]));
         }
         m_ref = m_run;
         m_ref_o = m_run_o;
