@@ -252,6 +252,20 @@ def test_edge_lengths():
     _case(1, 129, 4, 2, 128, torch.float32, False, 32, 8.0, [0.0, 1.0], seed=13)
 
 
+@pytest.mark.parametrize("L", [128, 191, 192, 193, 256, 320, 321])
+def test_two_unit_full_tile_loop_boundaries(L):
+    """Two units per workgroup (paired GQA heads, causal; neighbouring query blocks, non-causal)
+    run the steps whose copies are all full key tiles in a loop of their own, then the rest:
+    lengths at and around multiples of the 64-key tile change how many steps each loop takes
+    (none, one pair, several, with and without a partial last tile), also under a window."""
+    lams = [0.0, 16 / L, 1.0]
+    _case(1, L, 4, 2, 128, torch.bfloat16, True, 128, 16.0, lams, seed=6100 + L,
+          cluster_len=64, sinks=8)
+    _case(2, L, 3, 3, 64, torch.bfloat16, False, 128, 16.0, lams, seed=6200 + L, cluster_len=64)
+    _case(1, L, 4, 2, 128, torch.bfloat16, True, 128, 16.0, lams[:2], seed=6300 + L,
+          cluster_len=64, window=130)
+
+
 def _sampled_full_size(q, k, v, causal, lam, units, what, window=0):
     res = _run_gpu(q, k, v, causal=causal, lam=lam, window=window)
     ref = oracle.prefill(q, k, v, causal=causal, block_r=res["br"], block_c=res["bc"],
