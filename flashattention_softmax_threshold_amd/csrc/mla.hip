@@ -15,7 +15,7 @@
 //   * the K tile (64 x 576 bf16, 72 KB) goes from HBM straight into LDS (global_load_lds_dwordx4,
 //     two stages); the next tile's loads are issued between the MFMAs of this tile's scores;
 //   * S^T (32 keys x 32 heads) = K Q^T with v_mfma_f32_32x32x16_bf16 over 36 k-steps: A = K rows
-//     of the wave's key half from LDS, B = the wave's 32 query rows kept in registers (144 VGPRs);
+//     of the wave's key half from LDS, B = the wave's 32 query rows kept in registers (144 AGPRs);
 //   * the waves publish their partial row maxima through LDS; after one barrier every wave forms
 //     the tile maxima and running maxima of all 64 rows of the unit and takes the test itself,
 //     so all four reach the same decision without exchanging votes;
@@ -149,6 +149,10 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
       qf[s] = row_ok ? *(const bf16x8_t *)(qrow + 16 * s + 8 * hh) : (bf16x8_t)(__bf16)0.f;
+    // Q is only ever an MFMA B operand, which may come from AGPRs: kept there, it leaves the
+    // VGPRs to O^T and the K and V^T fragments read ahead of their MFMAs.
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) asm volatile("" : "+a"(qf[s]));
   }
 
   // Tile loads: wave load nn < 16 copies latent row i = wv + 4 nn (chunk L ^ lat_swz(i) of the
@@ -277,6 +281,9 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
       } else if constexpr (MODE == 2) {
         if (s2 & 1) issue_one(next_tile, st ^ 1, s2 >> 1, next_pages);
       }
+      // Without this the scheduler sinks the K reads next to their MFMAs to save registers,
+      // and each MFMA waits out an LDS read latency.
+      __builtin_amdgcn_sched_barrier(0);
     }
     return sacc;
   };
@@ -309,8 +316,8 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   // O^T (this wave's 128 columns, both row groups) += V^T P^T over the tile's 64 keys: k-step ks
   // (keys 16 ks .. 16 ks + 15) takes as B the bf16 P fragments of those keys for row groups 0 and
   // 1, as published by waves 2 (ks / 2) and 2 (ks / 2) + 1, and as A 4 column blocks of V^T
-  // (transpose reads of the row-major tile, stage st), each read once, RA reads ahead, for two
-  // MFMAs. The read of column block db, rows 16 ks + vrow (and + 8) is at a per-lane offset plus
+  // (transpose reads of the row-major tile, stage st), each read once, RA reads ahead (held there
+  // by a scheduling barrier per fragment), for two MFMAs. The read of column block db, rows 16 ks + vrow (and + 8) is at a per-lane offset plus
   // 16384 ks: with f = lat_swz(vrow), chunk 16 w + 4 db + vcb sits at 16 w + ((4 db + vcb) ^ f),
   // and the row + 8 at f ^ 2.
   uint32_t v_off[kDvBlocks], v_off_hi[kDvBlocks];
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
   }
   auto pv = [&](int st) {
     constexpr int NM = 4 * kDvBlocks;  // 16 V^T fragments: (ks, db) = (m / 4, m % 4)
-    constexpr int RA = 2;
+    constexpr int RA = 3;
     // B operands: P of row group r, k-step ks, as published by wave r + 2 (ks / 2).
     bf16x8_t pb[2][4];
 #pragma unroll
@@ -353,6 +360,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeParams p) {
       for (int r = 0; r < 2; ++r)
         oacc[r][m % kDvBlocks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             va[m % (RA + 1)], pb[r][m / kDvBlocks], oacc[r][m % kDvBlocks], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
