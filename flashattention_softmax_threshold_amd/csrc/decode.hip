@@ -234,12 +234,31 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void decode_gqa_kernel(Decode
     float mt = -INFINITY;
     const bool next_k = have && t + 4 < t_end;
     if (have) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        sacc[kb] = (f32x4_t)0.f;
+      if constexpr (PAGED) {
+        // Paged: all 4 x STEPS K fragments are requested first and the MFMAs take them k-step by
+        // k-step across the 4 key blocks (each block's sum keeps its order, so the result is the
+        // same); faster by 2-3 % here, but slower by as much on a contiguous cache.
+        bf16x8_t kf[4 * STEPS];
 #pragma unroll
         for (int s = 0; s < STEPS; ++s)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdk(kb, s), qf[s], sacc[kb], 0, 0, 0);
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) kf[4 * s + kb] = rdk(kb, s);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sacc[kb] = (f32x4_t)0.f;
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[4 * s + kb], qf[s], sacc[kb], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          sacc[kb] = (f32x4_t)0.f;
+#pragma unroll
+          for (int s = 0; s < STEPS; ++s)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdk(kb, s), qf[s], sacc[kb], 0, 0, 0);
+        }
       }
       if ((t + 1) * kBlockC > seq_len || t * kBlockC < first_key) {
 #pragma unroll
