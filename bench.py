@@ -73,7 +73,7 @@ def _parse():
                          "workload only (profiling runs isolate one kernel this way)")
     ap.add_argument("--a", type=float, default=None,
                     help="prefill / decode / mla parts: time only lambda = a / L instead of the "
-                         "sweep")
+                         "sweep; window part: only lambda = a / W")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes three times "
                          "(the reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -783,7 +783,8 @@ def _window_part(F, torch, args, dev, stream, out):
     dense_flops = 4.0 * Hq * d * sum(min(i + 1, W) for i in range(L))
     pts = []
     ms0 = None
-    for a in (0.0, 16.0):
+    a_list = (0.0, 16.0) if args.a is None else (args.a,)  # --a: one threshold (counter passes)
+    for a in a_list:
         lam = a / W
         ms = _time_auto(lambda: F.blasst_attn_prefill(q, k, v, causal=True, lam=lam, o=o,  # noqa
                                                       window=W, stream=stream),
@@ -796,7 +797,8 @@ def _window_part(F, torch, args, dev, stream, out):
         ex = tile_flops * (2 * vis - sk) / (ms * 1e-3) / 1e12
         pts.append({"lambda": f"{a:g}/W", "ms": ms, "skip_fraction": sk / vis,
                     "dense_tflops": dense_flops / (ms * 1e-3) / 1e12, "executed_tflops": ex,
-                    "mfma_frac": ex / BF16_PEAK_TFLOPS, "speedup_vs_lambda0": ms0 / ms})
+                    "mfma_frac": ex / BF16_PEAK_TFLOPS,
+                    "speedup_vs_lambda0": (ms0 / ms) if ms0 else None})
         _progress(f"window prefill a={a:g}: {ms:.4f} ms")
     out["window_prefill"] = {"workload": f"causal GQA prefill B1 Hq32/Hkv8 L8192 d128 bf16, "
                                          f"window {W}, tile {br}x{bc}", "points": pts}
@@ -813,7 +815,7 @@ def _window_part(F, torch, args, dev, stream, out):
                       dtype=torch.uint8, device=dev)
     tile_bytes = bcd * D["d"] * 2
     dpts = []
-    for a in (0.0, 16.0):
+    for a in a_list:
         lam = a / Wd
         ms = _time_auto(lambda: F.blasst_attn_decode(qd, kd, vd, kv_len=kvl, lam=lam, o=od,  # noqa
                                                      workspace=wsd, window=Wd, stream=stream),
