@@ -258,10 +258,9 @@ DecodeKind decode_kind(const blasst_decode_args *a) {
   return kNone;
 }
 
-// Split count chosen by the library: enough work units to give every CU about two of them,
-// but at least 8 tiles per split.
-int auto_splits(int units, int n_tiles) {
-  const int target = 2 * 256;
+// Split count chosen by the library: at least `target` work units (every CU about two of them
+// by default), but at least 8 tiles per split.
+int auto_splits(int units, int n_tiles, int target = 2 * 256) {
   if (units >= target || n_tiles <= 8) return 1;
   int s = ceil_div(target, units);
   const int max_s = n_tiles / 8 > 0 ? n_tiles / 8 : 1;
@@ -297,15 +296,18 @@ blasst_status blasst_decode_plan(const blasst_decode_args *a, int32_t *block_r, 
     br = a->block_r ? a->block_r : (group < 16 ? group : 16);
     if (br < 1 || br > 16) return BLASST_ERR_UNSUPPORTED;
   } else {
-    br = a->block_r ? a->block_r : 64;
-    if (br != 64) return BLASST_ERR_UNSUPPORTED;
+    // MLA: a unit of up to 128 heads (one workgroup fills a CU) when the group has more than 64,
+    // else the 64-head kernel.
+    br = a->block_r ? a->block_r : (group > 64 ? 128 : 64);
+    if (br != 64 && br != 128) return BLASST_ERR_UNSUPPORTED;
   }
+  const bool wide_mla = kind == kMla && br > 64 && group > 64;
   if (br > group) br = group;
   int s = a->num_splits;
   if (s < 0) return BLASST_ERR_INVALID_ARG;
   if (s == 0) {
     const int units = a->batch * a->heads_kv * ceil_div(group, br);
-    s = auto_splits(units > 0 ? units : 1, split_span(a, bc));
+    s = auto_splits(units > 0 ? units : 1, split_span(a, bc), wide_mla ? 256 : 2 * 256);
   }
   if (s > 256) return BLASST_ERR_UNSUPPORTED;
   *block_r = br;
@@ -399,6 +401,8 @@ blasst_status decode_with_workspace(const blasst_decode_args *a, void *workspace
   hipError_t err;
   if (kind == kGqa) {
     err = blasst::launch_decode_gqa(p, a->head_dim_qk, (hipStream_t)stream);
+  } else if (br > 64) {
+    err = blasst::launch_decode_mla128(p, (hipStream_t)stream);
   } else {
     err = blasst::launch_decode_mla(p, (hipStream_t)stream);
   }

@@ -73,6 +73,8 @@ struct DecodeParams {
 
 hipError_t launch_decode_gqa(const DecodeParams &p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeParams &p, hipStream_t stream);
+// MLA with up to 128 query heads per unit (mla128.hip).
+hipError_t launch_decode_mla128(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_split_combine(const DecodeParams &p, int head_dim_v, hipStream_t stream);
 
 }  // namespace blasst

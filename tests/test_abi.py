@@ -223,15 +223,34 @@ def test_decode_rejects_bad_arguments_before_launch():
 
 
 def test_decode_plan_with_window_splits_the_window_span():
-    # MLA shape, 32 sequences x 2 row blocks = 64 units: without a window the 1024 tiles of 64K
-    # keys get 8 splits of 128 tiles; a 4096-key window touches at most 65 tiles, cut 8 ways
-    # (ceil(65 / 8) = 9 tiles per split), and a short window with few tiles is not split.
+    # MLA shape with the 64-head kernel, 32 sequences x 2 row blocks = 64 units: without a window
+    # the 1024 tiles of 64K keys get 8 splits of 128 tiles; a 4096-key window touches at most 65
+    # tiles, cut 8 ways (ceil(65 / 8) = 9 tiles per split), and a short window with few tiles is
+    # not split.
     q, k = _meta((32, 128, 576)), _meta((32, 65536, 1, 576))
     v = k[..., :512]
-    assert F.blasst_decode_plan(q, k, v) == (64, 64, 8)
-    assert F.blasst_decode_plan(q, k, v, window=4096) == (64, 64, 8)
-    assert F.blasst_decode_plan(q, k, v, window=300) == (64, 64, 1)
-    assert F.blasst_decode_workspace_size(q, k, v, window=300) == 0
+    assert F.blasst_decode_plan(q, k, v, block_r=64) == (64, 64, 8)
+    assert F.blasst_decode_plan(q, k, v, block_r=64, window=4096) == (64, 64, 8)
+    assert F.blasst_decode_plan(q, k, v, block_r=64, window=300) == (64, 64, 1)
+    assert F.blasst_decode_workspace_size(q, k, v, block_r=64, window=300) == 0
+    # The default for 128 heads: one unit of 128 heads per sequence and split (32 units), split
+    # until the 256 CUs each hold one workgroup (8 splits), the same window rules.
+    assert F.blasst_decode_plan(q, k, v) == (128, 64, 8)
+    assert F.blasst_decode_plan(q, k, v, window=4096) == (128, 64, 8)
+    assert F.blasst_decode_plan(q, k, v, window=300) == (128, 64, 1)
+
+
+def test_mla_plan_row_blocks():
+    # 64 or fewer heads: the 64-head kernel; more: up to 128 per unit; other sizes unsupported.
+    v_of = lambda k: k[..., :512]  # noqa: E731
+    for hq, want in ((16, 16), (64, 64), (96, 96), (128, 128), (256, 128)):
+        q, k = _meta((2, hq, 576)), _meta((2, 4096, 1, 576))
+        assert F.blasst_decode_plan(q, k, v_of(k))[0] == want, hq
+    q, k = _meta((2, 128, 576)), _meta((2, 4096, 1, 576))
+    assert F.blasst_decode_plan(q, k, v_of(k), block_r=64)[0] == 64
+    with pytest.raises(F.BlasstError) as e:
+        F.blasst_decode_plan(q, k, v_of(k), block_r=32)
+    assert e.value.status == F.BLASST_ERR_UNSUPPORTED
 
 
 # ------------------------------------------------------------------------------------------

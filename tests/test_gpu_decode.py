@@ -193,26 +193,31 @@ def test_layouts_equal_heads_major_bitwise(Hq, Hkv, D, splits):
     assert torch.all(o_wide[:, :, D:] == 3.0), "columns past d_v were written"
 
 
-def test_mla_small_lengths_and_splits():
-    """MLA shape: 128 query heads on one latent KV head, d_qk 576, V = the first 512 columns."""
+@pytest.mark.parametrize("block_r", [0, 64])
+def test_mla_small_lengths_and_splits(block_r):
+    """MLA shape: 128 query heads on one latent KV head, d_qk 576, V = the first 512 columns;
+    one unit of 128 heads (the default) or two of 64."""
     L = 700
     lams = [0.0, 16 / L, 1.0]
     _case(2, 128, 1, L, 576, [700, 321], lams[:2], (1, 3), 1.0, True, seed=31, Dv=512,
-          cluster_len=128)
+          cluster_len=128, block_r=block_r)
     assert _case(2, 128, 1, L, 576, [700, 130], lams, (1, 4), 16.0, True, seed=32, Dv=512,
-                 cluster_len=128) > 0
+                 cluster_len=128, block_r=block_r) > 0
 
 
-@pytest.mark.parametrize("Hq", [16, 40, 100])
-def test_mla_partial_head_blocks(Hq):
-    """MLA with head counts that leave row groups empty (16: the second 32-head group of the only
-    block), half full (40) or a partial second block (100: heads 64..99): every wave's P.V
-    covers both row groups of its block, so invalid rows must neither leak into valid ones nor be
-    written."""
+@pytest.mark.parametrize("Hq,block_r", [(16, 0), (40, 0), (100, 64), (100, 0), (72, 0),
+                                        (200, 0)])
+def test_mla_partial_head_blocks(Hq, block_r):
+    """MLA with head counts that leave row groups empty or partial. 64-head kernel: 16 (the
+    second 32-head group of the only block empty), 40 (half full), 100 with blocks of 64 (a
+    partial second block, heads 64..99): every wave's P.V covers both row groups of its block.
+    128-head kernel: 100 (the last wave's rows 96..127 partly empty) and 72 (waves 2 and 3
+    with 8 and no valid rows), 200 (a second block of 72 heads). Invalid rows must neither
+    leak into valid ones nor be written, and must not take part in the vote."""
     L = 600
     lams = [0.0, 16 / L, 1.0]
     assert _case(2, Hq, 1, L, 576, [600, 257], lams, (1, 3), 16.0, True, seed=3300 + Hq, Dv=512,
-                 cluster_len=128) > 0
+                 cluster_len=128, block_r=block_r) > 0
 
 
 def test_gqa_sliding_window_lengths_and_splits():
@@ -226,10 +231,11 @@ def test_gqa_sliding_window_lengths_and_splits():
         assert n > 0 or w == 1
 
 
-def test_mla_sliding_window_and_splits():
+@pytest.mark.parametrize("block_r", [0, 64])
+def test_mla_sliding_window_and_splits(block_r):
     L = 900
     assert _case(2, 128, 1, L, 576, [900, 300], [0.0, 16 / 400, 1.0], (1, 3), 16.0, True,
-                 seed=44, Dv=512, cluster_len=128, window=400) > 0
+                 seed=44, Dv=512, cluster_len=128, window=400, block_r=block_r) > 0
 
 
 def test_paged_gqa_sliding_window_equals_contiguous_bitwise():
@@ -266,7 +272,7 @@ def test_mla_decode_full_size_sampled():
 # output must equal the contiguous call on the same keys bit for bit.
 # ------------------------------------------------------------------------------------------
 def _paged_vs_contiguous(B, Hq, Hkv, L, D, Dv, kv_len, page_sizes, lams, splits, beta, share, seed,
-                         cluster_len=100, window=0, heads_major=False):
+                         cluster_len=100, window=0, heads_major=False, block_r=0):
     need_gpu()
     mla = Dv != D
     q, k, v, kvl = decode_inputs(B=B, Hq=Hq, Hkv=Hkv, L=L, d_qk=D, d_v=Dv, cluster_len=cluster_len,
@@ -278,9 +284,10 @@ def _paged_vs_contiguous(B, Hq, Hkv, L, D, Dv, kv_len, page_sizes, lams, splits,
             for lam in lams:
                 what = f"paged decode B{B} H{Hq}/{Hkv} L{L} d{D}/{Dv} page {ps} S={S} lam={lam}"
                 print(what, flush=True)
-                ref = _run_gpu(q, k, v, kvl, lam=lam, num_splits=S, window=window)
+                ref = _run_gpu(q, k, v, kvl, lam=lam, num_splits=S, window=window,
+                               block_r=block_r)
                 got = _run_gpu(q, kp, vp, kvl, lam=lam, num_splits=S, block_table=table,
-                               max_kv_len=L, window=window)
+                               max_kv_len=L, window=window, block_r=block_r)
                 assert got["splits"] == ref["splits"]
                 assert torch.equal(got["o"], ref["o"]), what
                 assert np.array_equal(got["lse"].cpu().numpy(), ref["lse"].cpu().numpy()), what
@@ -317,7 +324,8 @@ def test_paged_gqa_against_oracle():
     assert abs(res["counters"][1] - ref.skipped) <= band_mism
 
 
-def test_paged_mla_equals_contiguous_bitwise():
+@pytest.mark.parametrize("block_r", [0, 64])
+def test_paged_mla_equals_contiguous_bitwise(block_r):
     _paged_vs_contiguous(B=2, Hq=128, Hkv=1, L=700, D=576, Dv=512, kv_len=[700, 129],
                          page_sizes=(16, 64), lams=(0.0, 16 / 700), splits=(1, 2), beta=4.0,
-                         share=True, seed=8300, cluster_len=128)
+                         share=True, seed=8300, cluster_len=128, block_r=block_r)
