@@ -34,6 +34,7 @@
 #include <math.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace blasst {
 namespace {
@@ -105,6 +106,17 @@ __device__ __forceinline__ void o_mfma(int cb, const bf16x8_t &a, const bf16x8_t
 __device__ __forceinline__ void o_scale(int cb, float alpha) { BLASST_AGPR_CASES(scale, alpha) }
 __device__ __forceinline__ void o_read(int cb, float (&x)[16]) { BLASST_AGPR_CASES(read, x) }
 #undef BLASST_AGPR_CASES
+
+// f(std::integral_constant<int, I>) for I = 0 .. N - 1, in order: indices that must be
+// compile-time constants (register blocks, array slots) whatever the unroller decides.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 template <bool PAGED>
 __global__ __launch_bounds__(256, 1) void decode_mla128_kernel(DecodeParams p) {
@@ -302,19 +314,41 @@ __global__ __launch_bounds__(256, 1) void decode_mla128_kernel(DecodeParams p) {
   // transposed reads, rows 16 ks + vrow and + 8; with f = lat_swz(vrow), chunk 4 cb + vcb of the
   // latent row sits at 16 (cb / 4) + ((4 (cb % 4) + vcb) ^ f), and the row + 8 at f ^ 2. Four
   // per-lane offsets each; cb / 4 and ks are constant offsets.
-  // O^T += V^T P^T over the tile's 64 keys: k-step ks takes as B the bf16 P of the score
-  // registers 8 (ks % 2) .. + 7 of key block ks / 2 (this lane's keys 16 ks + 8 (e / 4) + 4 hh +
-  // e % 4, the same keys the transposed V reads give its A rows), and as A the 16 column blocks
-  // of V^T, each read once, RA fragments ahead. The A operand of k-step ks and column block cb
-  // is two transposed reads, rows 16 ks + vrow and + 8; with f = lat_swz(vrow), chunk
-  // 4 cb + vcb of the latent row sits at 16 (cb / 4) + ((4 (cb % 4) + vcb) ^ f), and the row + 8
-  // at f ^ 2: four per-lane offsets each, cb / 4 and ks constant offsets.
-  auto pv = [&](int st, const bf16x8_t (&pb)[4]) {
+  // O^T += V^T P^T over the tile's 64 keys, with P formed on the way. P = 2^(s - m_ref) in bf16
+  // of k-step ks is the B operand of that k-step: score registers 8 (ks % 2) .. + 7 of key block
+  // ks / 2, this lane's keys 16 ks + 8 (e / 4) + 4 hh + e % 4 -- the same keys the transposed V
+  // reads give its A rows. P of k-step 0 is formed first; P of k-step ks + 1 one element per MFMA
+  // slot between the 16 MFMAs of k-step ks (the exponentials run while the matrix pipe works).
+  // The A operand of k-step ks and column block cb is two transposed reads, rows 16 ks + vrow and
+  // + 8; with f = lat_swz(vrow), chunk 4 cb + vcb of the latent row sits at
+  // 16 (cb / 4) + ((4 (cb % 4) + vcb) ^ f), and the row + 8 at f ^ 2: four per-lane offsets
+  // each, cb / 4 and ks constant offsets. Returns this lane's part of the row sum of the rounded
+  // P.
+  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+  auto pv = [&](int st, const f32x16_t &s0, const f32x16_t &s1) {
     constexpr int NM = 4 * kCB;  // (ks, cb) = (m / 16, m % 16)
     constexpr int RA = RA_;
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    auto p_elem = [&](int ks, int e) {
+      const f32x16_t &sa = (ks < 2) ? s0 : s1;
+      return exp2_fast(fmaf(sa[8 * (ks & 1) + e], p.scale_log2, -m_use));
+    };
+    float ps0 = 0.f, ps1 = 0.f;
+    // Rounds 8 elements to a bf16 B operand and adds them (as rounded) to the row sums.
+    auto pack = [&](const float (&x)[8]) {
+      bf16x8_t pk;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[e] = (__bf16)x[e];
+      const bf16x2_t x0 = {pk[0], pk[1]}, x1 = {pk[2], pk[3]};
+      const bf16x2_t x2 = {pk[4], pk[5]}, x3 = {pk[6], pk[7]};
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(x0, one, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(x1, one, ps1, false);
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(x2, one, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, ps1, false);
+      return pk;
+    };
     const char *vl = smem[st];
-    // V^T read offsets of this lane (see above), formed here so that they are not held across
-    // the scores.
+    // V^T read offsets of this lane, formed here so that they are not held across the scores.
     uint32_t v_off[4], v_off_hi[4];
     {
       int ln = lane;
@@ -340,35 +374,25 @@ __global__ __launch_bounds__(256, 1) void decode_mla128_kernel(DecodeParams p) {
     bf16x8_t va[RA + 1];
 #pragma unroll
     for (int m = 0; m < RA; ++m) va[m] = rdv(m);
+    bf16x8_t pb[4];
+    {
+      float x[8];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      if (m + RA < NM) va[(m + RA) % (RA + 1)] = rdv(m + RA);
-      o_mfma(m % kCB, va[m % (RA + 1)], pb[m / kCB]);
+      for (int e = 0; e < 8; ++e) x[e] = p_elem(0, e);
+      pb[0] = pack(x);
+    }
+    float xn[8];
+    static_for<NM>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int ks = m / kCB, cb = m % kCB;
+      if constexpr (m + RA < NM) va[(m + RA) % (RA + 1)] = rdv(m + RA);
+      agpr::mfma<cb>(va[m % (RA + 1)], pb[ks]);
+      if constexpr (ks < 3) {
+        if constexpr (cb < 8) xn[cb] = p_elem(ks + 1, cb);
+        if constexpr (cb == 8) pb[ks + 1] = pack(xn);
+      }
       __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // P = 2^(s - m_ref) in bf16 (B operands of P.V) and this lane's part of the row sum of the
-  // rounded P.
-  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
-  auto make_p = [&](const f32x16_t &s0, const f32x16_t &s1, bf16x8_t (&pb)[4]) {
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const f32x16_t &sa = (ks < 2) ? s0 : s1;
-      bf16x8_t pk;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pk[e] = (__bf16)exp2_fast(fmaf(sa[8 * (ks & 1) + e], p.scale_log2, -m_use));
-      const bf16x2_t x0 = {pk[0], pk[1]}, x1 = {pk[2], pk[3]};
-      const bf16x2_t x2 = {pk[4], pk[5]}, x3 = {pk[6], pk[7]};
-      ps0 = __builtin_amdgcn_fdot2_f32_bf16(x0, one, ps0, false);
-      ps1 = __builtin_amdgcn_fdot2_f32_bf16(x1, one, ps1, false);
-      ps0 = __builtin_amdgcn_fdot2_f32_bf16(x2, one, ps0, false);
-      ps1 = __builtin_amdgcn_fdot2_f32_bf16(x3, one, ps1, false);
-      pb[ks] = pk;
-    }
+    });
     return ps0 + ps1;
   };
 
@@ -429,10 +453,6 @@ __global__ __launch_bounds__(256, 1) void decode_mla128_kernel(DecodeParams p) {
       for (int o = 32; o >= 1; o >>= 1) dm = fmaxf(dm, __shfl_xor(dm, o));
       if (lane == 0) sMarg[wv] = dm;
     }
-    // P with the current reference max, formed before the vote barrier; a kept tile that moves
-    // this wave's reference max forms it again.
-    bf16x8_t pb[4];
-    float ps = make_p(s0, s1, pb);
     __syncthreads();
     const bool keep = (sVote[0] | sVote[1] | sVote[2] | sVote[3]) != 0;
     if (bookkeeper) {
@@ -453,10 +473,8 @@ __global__ __launch_bounds__(256, 1) void decode_mla128_kernel(DecodeParams p) {
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) o_scale(cb, alpha);
         m_ref = m_run;
-        ps = make_p(s0, s1, pb);
       }
-      l_part += ps;
-      pv(j & 1, pb);
+      l_part += pv(j & 1, s0, s1);
     }
   }
 
