@@ -636,7 +636,9 @@ def _mla_part(F, torch, args, dev, stream, out):
                                      f"centre gain {MLA_BETA}, tile {brm}x{bcm}, {sm} splits",
                          "points": mla, "skip_curve": curve, "literal_gain1": gain1,
                          "traffic_lambda_16/L": _traffic_from_profile(
-                             "mla.hip", "decode_mla_B32_L65536_hbm_counters.json")}
+                             "mla128.hip" if brm > 64 else "mla.hip",
+                             "decode_mla128_B32_L65536_hbm_counters.json" if brm > 64
+                             else "decode_mla_B32_L65536_hbm_counters.json")}
 
 
 def _headline_part(F, torch, args, dev, stream, out):
