@@ -63,12 +63,10 @@ constexpr int kBR = 128;                            // query heads per unit
 // O and l are rescaled only when some row's max has grown by more than this (base-2 units)
 // since the last rescale: P = 2^(s - m_ref) stays below 2^8; the algebra is exact.
 constexpr float kRescaleSlack = 8.f;
-#ifndef KPF_
-#define KPF_ 2
-#endif
-#ifndef RA_
-#define RA_ 4
-#endif
+// LDS read-ahead: K fragments of the scores 2 k-steps (4 fragments) ahead, V^T fragments of P.V
+// 4 MFMAs ahead (deeper read-ahead measured no faster; 3 k-steps makes the paged instance spill).
+constexpr int kKpf = 2;
+constexpr int kRa = 4;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
@@ -262,7 +260,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla128_kernel(DecodeParams p) {
   auto compute_s = [&](auto mode_c, int st, int next_tile, int next_pages, f32x16_t &s0,
                        f32x16_t &s1) {
     constexpr int MODE = decltype(mode_c)::value;
-    constexpr int KPF = KPF_;
+    constexpr int KPF = kKpf;
     const char *tb = (const char *)(Kg + (int64_t)next_tile * kBlockC * p.k_ss);
     const char *cur = tb + (int64_t)wv * row_bytes;
     s0 = (f32x16_t)0.f;
@@ -327,7 +325,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla128_kernel(DecodeParams p) {
   const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
   auto pv = [&](int st, const f32x16_t &s0, const f32x16_t &s1) {
     constexpr int NM = 4 * kCB;  // (ks, cb) = (m / 16, m % 16)
-    constexpr int RA = RA_;
+    constexpr int RA = kRa;
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
     auto p_elem = [&](int ks, int e) {
       const f32x16_t &sa = (ks < 2) ? s0 : s1;
