@@ -437,13 +437,15 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
       if (j + 1 < n_tiles) issue_k(j + 1, (j + 1) & 1);
       issue_v(j, j & 1);
     }
-    const int keep_prev = decision(j - 1, vt);
     const float m_prev = m_run;
     compute_s(full_c, j & 1, cur, NH == 2 ? j : -1);
     if constexpr (FULL) {
       kt_run += k_tile_bytes;
       vt_run += v_tile_bytes;
     }
+    // The decision on tile j - 1 is taken only now, so the scores' first K reads do not wait
+    // behind the vote read (one LDS round trip at the top of the step instead of two).
+    const int keep_prev = decision(j - 1, vt);
     mask_tile(j, cur);
     if (keep_prev) {
       rescale_to(m_prev);
