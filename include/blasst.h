@@ -215,8 +215,10 @@ blasst_status blasst_prefill_tiles(const blasst_prefill_args *args, int32_t *blo
  * shape) the value tile is read from the key tile already on chip, so skipping saves compute.
  *
  * Supported: BLASST_BF16; GQA kernel: head_dim_qk == head_dim_v == 128 (or 64), block_c 64,
- * block_r <= 16; MLA kernel: head_dim_qk 576, head_dim_v 512, heads_kv 1, v == k, block_c 64,
- * block_r 64. tile_status / tile_margin:
+ * block_r <= 16; MLA kernels: head_dim_qk 576, head_dim_v 512, heads_kv 1, v == k, block_c 64,
+ * block_r 64 or 128 (0 = 128 when heads_q > 64, else 64; a block larger than heads_q is cut to
+ * heads_q). With block_r 128 one unit covers up to 128 heads and each K tile is read once for
+ * all of them. tile_status / tile_margin:
  * [batch, heads_kv, ceil(G / block_r), ceil(max_kv_len / block_c)], G = heads_q / heads_kv.
  *
  * Paged KV cache ("The Hitchhiker's Guide -- Phase 08", paged attention: a block table maps a
