@@ -206,13 +206,13 @@ def test_mla_small_lengths_and_splits(block_r):
 
 
 @pytest.mark.parametrize("Hq,block_r", [(16, 0), (40, 0), (100, 64), (100, 0), (72, 0),
-                                        (200, 0)])
+                                        (65, 0), (200, 0)])
 def test_mla_partial_head_blocks(Hq, block_r):
     """MLA with head counts that leave row groups empty or partial. 64-head kernel: 16 (the
     second 32-head group of the only block empty), 40 (half full), 100 with blocks of 64 (a
     partial second block, heads 64..99): every wave's P.V covers both row groups of its block.
-    128-head kernel: 100 (the last wave's rows 96..127 partly empty) and 72 (waves 2 and 3
-    with 8 and no valid rows), 200 (a second block of 72 heads). Invalid rows must neither
+    128-head kernel: 100 (the last wave's rows 96..127 partly empty), 72 (waves 2 and 3
+    with 8 and no valid rows), 65 (one valid row in wave 2), 200 (a second block of 72 heads). Invalid rows must neither
     leak into valid ones nor be written, and must not take part in the vote."""
     L = 600
     lams = [0.0, 16 / L, 1.0]
