@@ -244,7 +244,8 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
   // hides behind matrix work; the scheduling hints keep that order. With vj >= 0 the copies of
   // V_vj and K_{vj+1} are issued between the MFMAs (after the second and the fourth k-step): a
   // wave held up issuing them still has MFMAs in flight.
-  auto compute_s = [&](auto full_c, int st, f32x16_t *sacc, int vj = -1) {
+  auto compute_s = [&](auto full_c, int st, f32x16_t *sacc, int vj = -1,
+                       const int4 *votes = nullptr, int *vote_or = nullptr) {
     constexpr bool FULL = decltype(full_c)::value;
     constexpr int NS = D / 16;  // k-steps
     // The V copy goes out after k-step 1 and the K copy after k-step 3: both need four k-steps.
@@ -267,6 +268,11 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s][kb], qf[s], sacc[kb], 0, 0, 0);
+      // The unit's four vote words, read at the top of the step, folded into one wave-uniform
+      // word behind the first k-step (so the vote read's wait does not hold up the first K
+      // fragment reads, and only one scalar register carries it through the scores).
+      if (s == 1 && votes)
+        *vote_or = __builtin_amdgcn_readfirstlane(votes->x | votes->y | votes->z | votes->w);
       if constexpr (FULL) {
         if (s == 1) issue_full(vt_run, vj & 1, 1);
         if (s == 3) issue_full(kt_run, (vj + 1) & 1, 0);
@@ -332,8 +338,7 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
   // lane of the unit's first wave keeps its counts and observation outputs.
   const bool bookkeeper = wq == 0 && lane == 0 && unit_ok;
   auto read_votes = [&](int j) { return *(const int4 *)&sVote[j & 1][kNW * hs]; };
-  auto decision = [&](int j, int4 vt) {
-    const int keep = vt.x | vt.y | vt.z | vt.w;
+  auto decision = [&](int j, int keep) {
     if (bookkeeper) {
       ++visited;
       skipped += keep ? 0u : 1u;
@@ -438,14 +443,17 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
       issue_v(j, j & 1);
     }
     const float m_prev = m_run;
-    compute_s(full_c, j & 1, cur, NH == 2 ? j : -1);
+    int vote_or = 0;
+    compute_s(full_c, j & 1, cur, NH == 2 ? j : -1, &vt, &vote_or);
     if constexpr (FULL) {
       kt_run += k_tile_bytes;
       vt_run += v_tile_bytes;
     }
-    // The decision on tile j - 1 is taken only now, so the scores' first K reads do not wait
-    // behind the vote read (one LDS round trip at the top of the step instead of two).
-    const int keep_prev = decision(j - 1, vt);
+    // The decision on tile j - 1 is taken only now: the vote words are folded into one word
+    // inside the scores, so the first K reads do not wait behind the vote read (one LDS round
+    // trip at the top of the step instead of two) and the four words are not held through the
+    // scores (which would push the two-unit kernel past 256 registers).
+    const int keep_prev = decision(j - 1, vote_or);
     mask_tile(j, cur);
     if (keep_prev) {
       rescale_to(m_prev);
@@ -462,7 +470,8 @@ __global__ __launch_bounds__(kNT * NH, 2 / NH) void prefill_mfma_kernel(PrefillP
   auto finish = [&](const f32x16_t *last) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (decision(n_tiles - 1, read_votes(n_tiles - 1))) {
+    const int4 vl = read_votes(n_tiles - 1);
+    if (decision(n_tiles - 1, vl.x | vl.y | vl.z | vl.w)) {
       rescale_to(m_run);
       exp_pv(last, (n_tiles - 1) & 1);
     }
